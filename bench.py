@@ -1,0 +1,212 @@
+"""Benchmark: one serving step of the KDA engine on the mixed 16384-token batch.
+
+A step is the whole hot path over one packed batch -- 6 chunked prefills (lognormal lengths,
+16316 tokens), 32 single-token decodes and 4 speculative verifies of 1+8 positions, issued by
+kda_mixed_batch, then the ReplaySSM commit of the verified sequences -- on H=32 heads
+(one GPU's share), d_k = d_v = 128, a pool of 512 fp32 state slots. Inputs are synthetic and
+seeded (kda_inputs.mixed_workload) and resident in HBM before timing starts.
+
+Prints one JSON line. `value` = tokens per second of the whole step (16384 / step time).
+`roofline` describes the dominant kernel (the chunked prefill), timed with HIP events on the
+stream the library launches on, in a second timed pass that issues the same launches one by
+one. `cpu_baseline` times the CPU oracle on a bounded sample (a subset of heads).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA tokens/s + achieved HBM GB/s (decode/verify), MFMA % (prefill), 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16
+
+# Algorithmic bytes (d = 128, fp32 state, bf16 q/k/v/o, fp32 a and b).
+D = 128
+STATE_B = D * D * 4
+TOK_IN_B = 3 * D * 2 + D * 4 + 4            # q, k, v bf16 + a fp32 + b fp32
+TOK_OUT_B = D * 2                           # o bf16
+RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
+
+
+def prefill_bytes(n_tok, H, n_out, n_init=0, n_ckpt=0):
+    return n_tok * H * (TOK_IN_B + TOK_OUT_B) + (n_out + n_init + n_ckpt) * H * STATE_B
+
+
+def prefill_flops(n_tok, H, C=64):
+    # chunked form, triangle-exact: three d x d state contractions per token (K~S, Q~S,
+    # Kbar^T W), four C x C x d triangular products per chunk, the triangular solve.
+    return n_tok * H * (6 * D * D + 4 * D * C + C * C / 3)
+
+
+def decode_bytes(B, H):
+    return B * H * (2 * STATE_B + TOK_IN_B + TOK_OUT_B)
+
+
+def verify_bytes(B, P, H):
+    return B * H * (STATE_B + P * (TOK_IN_B + TOK_OUT_B + RING_ENTRY_B))
+
+
+def commit_bytes(n_replayed_total, B, H):
+    return B * H * 2 * STATE_B + n_replayed_total * H * RING_ENTRY_B
+
+
+def cpu_baseline(w, heads: int):
+    """The CPU oracle as it stands, on the same workload restricted to `heads` heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import KDAPool as OPool
+    H = w["H"]
+    hs = list(range(heads))
+    tok = w["tokens"]
+
+    def sub(x):
+        return x[:, hs] if x.ndim == 2 else x[:, hs, :]
+
+    npd = {n: sub(x) for n, x in tok.np.items()}
+    o = OPool(w["n_slots"], heads, D, D, w["ring_cap"])
+    for _ in range(w["n_slots"]):
+        o.alloc()
+    ds, vs, ps = w["decode_slots"], w["verify_slots"], w["prefill_slots"]
+    st = w["states"].double().numpy()[:, hs]
+    o.state[np.concatenate([ds, vs])] = st
+    n_pre, nd, P = w["cu_seqlens"][-1], w["n_decode"], w["n_pos"]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        o.prefill({n: x[:n_pre] for n, x in npd.items()}, w["cu_seqlens"],
+                  [-1] * len(ps), ps, [], 0)
+        o.decode({n: x[n_pre:n_pre + nd] for n, x in npd.items()}, ds)
+        o.verify({n: x[n_pre + nd:].reshape((len(vs), P) + x.shape[1:]) for n, x in npd.items()},
+                 vs)
+        o.commit(vs, w["n_accepted"])
+        dt = time.perf_counter() - t0
+    total_tok = int(w["cu_seqlens"][-1]) + nd + len(vs) * P
+    return {"value": total_tok * heads / H / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole mixed step (prefill, decode, verify, commit) on {heads} of "
+                      f"{H} heads, fp64 numpy, one thread; {dt:.1f} s of CPU time, scaled "
+                      f"to all {H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the KDA hot path shards by heads and sequences "
+              "with no exchange, and this build runs on a single MI355X (--gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kda_inputs as ki
+    import recurrent_linear_attention_amd as kda
+    from recurrent_linear_attention_amd import IndexArray
+
+    w = ki.mixed_workload(4)
+    H, P = w["H"], w["n_pos"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+    for _ in range(w["n_slots"]):
+        pool.kda_slot_alloc()
+    ds, vs, ps = w["decode_slots"], w["verify_slots"], w["prefill_slots"]
+    pool.state[np.concatenate([ds, vs]).tolist()] = w["states"].to(dev)
+    tok = w["tokens"]
+    q, k, v, a, b = (t.to(dev).contiguous() for t in (tok.q, tok.k, tok.v, tok.a, tok.b))
+    o = torch.empty((q.shape[0], H, D), dtype=torch.bfloat16, device=dev)
+    cu = IndexArray(w["cu_seqlens"], dev)
+    i_ps, i_ds, i_vs = IndexArray(ps, dev), IndexArray(ds, dev), IndexArray(vs, dev)
+    na = torch.from_numpy(w["n_accepted"]).to(dev)
+    n_pre, nd, nv = int(w["cu_seqlens"][-1]), w["n_decode"], w["n_verify"]
+    total_tok = n_pre + nd + nv * P
+
+    def step():
+        pool.kda_mixed_batch(q, k, v, a, b, cu, i_ps, i_ds, i_vs, P, o=o)
+        pool.kda_commit(i_vs, na)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_step_dev = e0.elapsed_time(e1) / args.steps
+
+    # Second timed pass: the same launches issued one by one, bracketed by events.
+    sl = lambda t, lo, hi: t[lo:hi]  # noqa: E731
+    dq, dk, dv, da, db, do = (sl(t, n_pre, n_pre + nd) for t in (q, k, v, a, b, o))
+    vq, vk, vv, va, vb, vo = (sl(t, n_pre + nd, total_tok).reshape((nv, P) + t.shape[1:])
+                              for t in (q, k, v, a, b, o))
+    pq, pk, pv, pa, pb, po = (sl(t, 0, n_pre) for t in (q, k, v, a, b, o))
+    names = ["prefill", "decode", "verify", "commit"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        E = ev[s]
+        E[0].record()
+        pool.kda_prefill(pq, pk, pv, pa, pb, cu, i_ps, o=po)
+        E[1].record()
+        pool.kda_decode(dq, dk, dv, da, db, i_ds, o=do)
+        E[2].record()
+        pool.kda_verify(vq, vk, vv, va, vb, i_vs, o=vo)
+        E[3].record()
+        pool.kda_commit(i_vs, na)
+        E[4].record()
+    torch.cuda.synchronize()
+    ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+          for i, n in enumerate(names)}
+    n_rep = int(np.sum(1 + w["n_accepted"]))
+    byts = {"prefill": prefill_bytes(n_pre, H, len(ps)), "decode": decode_bytes(nd, H),
+            "verify": verify_bytes(nv, P, H), "commit": commit_bytes(n_rep, nv, H)}
+    kernels = {n: {"ms": round(ms[n], 5), "alg_bytes": byts[n],
+                   "GBps": round(byts[n] / ms[n] / 1e6, 1),
+                   "hbm_frac": round(byts[n] / ms[n] / 1e6 / HBM_PEAK_GBS, 4)} for n in names}
+    pf = prefill_flops(n_pre, H)
+    kernels["prefill"]["alg_TFLOPs"] = round(pf / ms["prefill"] / 1e9, 2)
+    kernels["prefill"]["mfma_frac"] = round(pf / ms["prefill"] / 1e9 / MFMA_PEAK_TFLOPS, 4)
+    pre_gbs = byts["prefill"] / ms["prefill"] / 1e6
+    roofline = {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "prefill (chunked, all sequences of the batch in one launch)",
+                "alg_bytes_per_launch": byts["prefill"]}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.cpu_heads)
+
+    out = {"metric": METRIC, "value": round(total_tok / (ms_step / 1e3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "ms_per_step_device": round(ms_step_dev, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded, kda_inputs.mixed_workload)",
+           "config": {"workload": "mixed varlen batch: 6 prefills (lognormal lengths "
+                                  f"{w['lengths']}) + {nd} decodes + {nv} verifies of 1+{P - 1}, "
+                                  "then ReplaySSM commit",
+                      "tokens_per_step": total_tok, "heads": H, "d_k": D, "d_v": D,
+                      "chunk": 64, "pool_slots": w["n_slots"]},
+           "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) engine for the Kimi Delta Attention (KDA)
+ * fixed-size recurrent-state update.
+ *
+ * What is computed. The pages describe KDA as recurrent layers that keep a fixed-size state
+ * per head instead of a token-growing KV cache ("vLLM brings day-0 support to Moonshot's
+ * Kimi K3", section "Confirmed"; "vLLM lifts Kimi K3 throughput by up to 2.8x", section
+ * "Kimi K3 stresses the whole stack"). They print no equation; this library computes the
+ * gated delta rule with per-key-channel decay. Per head, with S a dk x dv fp32 matrix:
+ *
+ *     S_t = Diag(a_t) S_{t-1} - b_t k_t (k_t^T Diag(a_t) S_{t-1}) + b_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library never allocates
+ *     or frees device memory and never synchronises, except kda_read_device_error.
+ *   - Token tensors are dense row-major: q, k [n][H][dk] bf16; v [n][H][dv] bf16;
+ *     a [n][H][dk] fp32 (decay in (0,1)); b [n][H] fp32; o [n][H][dv] bf16.
+ *     Device pointers must be 16-byte aligned.
+ *   - Slot state is fp32 [num_slots][H][dk][dv] (row = key channel, column = value channel).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it only.
+ *   - Every call returns a kda_status; kda_last_error() gives a message for the last failure
+ *     on the calling thread. A failing call enqueues no device work and changes no host state.
+ *   - One pool is driven from one host thread at a time.
+ *   - Supported shapes: dk == dv in {16, 128}; prefill chunk 16 (dk 16) or 64 (dk 128).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_EINVAL = -1,        /* bad pointer, size, alignment or slot id                  */
+  KDA_ENOSLOT = -2,       /* pool exhausted                                           */
+  KDA_ESTATE = -3,        /* slot in the wrong state (free / idle / pending)          */
+  KDA_EUNSUPPORTED = -4,  /* shape or parameter this build does not instantiate       */
+  KDA_EWORKSPACE = -5,    /* workspace missing or too small                           */
+  KDA_EHIP = -6           /* a HIP runtime call failed                                */
+} kda_status;
+
+/* Device error bits, accumulated in the pool's device error word. */
+#define KDA_DEVERR_NACC_RANGE 1u   /* commit got n_accepted outside [0, verified-1]; clamped */
+#define KDA_DEVERR_SLOT_RANGE 2u   /* a device slot array held an id outside the pool; skipped */
+
+/* Pool geometry. ring_cap = positions a verify may hold (1 + max drafts), 1..64. */
+typedef struct {
+  int32_t num_slots, num_heads, dk, dv, ring_cap;
+} kda_pool_desc;
+
+/* Per-slot metadata kept in device memory (array of num_slots, 24 bytes each). */
+typedef struct {
+  int64_t pos;        /* tokens folded into the slot's state                          */
+  int32_t ring_head;  /* ring entry where the next verify starts writing              */
+  int32_t pending;    /* positions verified and not yet committed (0 = idle)          */
+  int32_t v_base;     /* ring_head at the last verify                                 */
+  int32_t v_npos;     /* positions written by the last verify                         */
+} kda_slot_meta;
+
+typedef struct kda_pool kda_pool;   /* opaque host object owned by the library */
+
+/* ---- sizes of the caller-owned device buffers ------------------------------------------ */
+/* state: num_slots*H*dk*dv*4 bytes.                                                         */
+size_t kda_state_bytes(const kda_pool_desc* desc);
+/* ReplaySSM ring, four sections, each 256-byte aligned, for every (slot, entry, head):
+ *   k bf16 [slot][ring_cap][H][dk] | v bf16 [..][dv] | a fp32 [..][dk] | b fp32 [slot][ring_cap][H]
+ * kda_ring_layout writes the byte offsets of the four sections into offsets[0..3].          */
+size_t kda_ring_bytes(const kda_pool_desc* desc);
+kda_status kda_ring_layout(const kda_pool_desc* desc, size_t offsets[4]);
+/* meta: kda_slot_meta[num_slots], then a uint32 device error word at
+ * kda_meta_error_offset(). The caller zero-fills the buffer before kda_pool_create.          */
+size_t kda_meta_bytes(const kda_pool_desc* desc);
+size_t kda_meta_error_offset(const kda_pool_desc* desc);
+
+/* ---- pool and slots (prefix-cache slot pool: "Kimi K3 is here: efficient day-0 support on
+ * vLLM", summary: one hybrid cache manages recurrent KDA state beside paged KV) ------------ */
+/* Validates desc and the three buffers and builds the free list. Host only; no device work.
+ * EINVAL on null/misaligned pointers or bad sizes, EUNSUPPORTED on dk/dv not instantiated.  */
+kda_status kda_pool_create(const kda_pool_desc* desc, void* state, void* ring, void* meta,
+                           kda_pool** out);
+/* Frees the host object only; the device buffers stay the caller's. */
+kda_status kda_pool_destroy(kda_pool* pool);
+/* Allocates the lowest free slot index. ENOSLOT when none is free. Host only; the slot's
+ * device state is whatever it last held -- call kda_slot_reset or write it by prefill.      */
+kda_status kda_slot_alloc(kda_pool* pool, int32_t* slot_out);
+/* EINVAL if the slot is not live; ESTATE if it has a pending verify.                       */
+kda_status kda_slot_free(kda_pool* pool, int32_t slot);
+/* Zeroes a live idle slot's state and metadata (one fill kernel, no memset node).           */
+kda_status kda_slot_reset(kda_pool* pool, int32_t slot, void* stream);
+/* Copies the state and pos of live idle slot src into live idle slot dst (dst ring pointer
+ * and pending cleared): a prefix-cache block export outside a prefill ("vLLM lifts Kimi K3
+ * throughput by up to 2.8x", section "KDA checkpoints stay inside the prefill").             */
+kda_status kda_slot_checkpoint(kda_pool* pool, int32_t src, int32_t dst, void* stream);
+
+/* ---- chunked prefill with in-pass checkpoint export ------------------------------------
+ * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "KDA checkpoints stay inside the
+ * prefill": the recurrent-state checkpoint is exported during the original prefill pass
+ * instead of splitting the prefill at the last cacheable block boundary.)
+ *
+ * Sequence i covers packed tokens [cu_seqlens[i], cu_seqlens[i+1]) of q/k/v/a/b/o. It starts
+ * from the state of init_slot[i] (or zeros if init_slot is NULL or init_slot[i] == -1),
+ * writes o for every token, writes its final state to out_slot[i] (which may equal
+ * init_slot[i]) with pos = init pos + length, and -- when ckpt_interval > 0 -- writes the
+ * state after every ckpt_interval of its tokens to the next entry of ckpt_slot
+ * (floor(len_i / ckpt_interval) entries per sequence, concatenated in sequence order), each
+ * with pos = init pos + boundary. All out and checkpoint slots must be live, idle and
+ * distinct, and no init slot may be another sequence's out or checkpoint slot.
+ * chunk must be the instantiated chunk for dk; ckpt_interval a multiple of chunk.
+ * Every h_* array is a host copy of the matching d_* device array (same contents); the host
+ * copies drive validation, the device copies drive the kernels. Zero-length sequences are
+ * allowed. The workspace is unused in this build (workspace_bytes may be 0).               */
+typedef struct {
+  const void* q; const void* k; const void* v;   /* bf16 */
+  const float* a; const float* b;
+  void* o;                                       /* bf16 */
+  int32_t n_seq, n_tok, chunk, ckpt_interval;
+  const int32_t* h_cu_seqlens; const int32_t* d_cu_seqlens;   /* [n_seq+1], starts at 0 */
+  const int32_t* h_init_slot;  const int32_t* d_init_slot;    /* [n_seq] or NULL        */
+  const int32_t* h_out_slot;   const int32_t* d_out_slot;     /* [n_seq]                */
+  const int32_t* h_ckpt_slot;  const int32_t* d_ckpt_slot;    /* concat, or NULL        */
+  void* workspace; size_t workspace_bytes;
+} kda_prefill_args;
+size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
+                                   int32_t chunk);
+kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);
+
+/* ---- decode and speculative verify ---------------------------------------------------- */
+/* Token tensors are [B][n_pos][H][d] (n_pos = 1 for decode); slots[B] are live, idle and
+ * distinct; h_slots / d_slots are host / device copies with the same contents.              */
+typedef struct {
+  const void* q; const void* k; const void* v;   /* bf16 */
+  const float* a; const float* b;
+  void* o;                                       /* bf16 [B][n_pos][H][dv] */
+  int32_t B;
+  const int32_t* h_slots; const int32_t* d_slots;
+} kda_step_args;
+
+/* One token per sequence against its slot: the state is read once, updated and written
+ * back in place; pos += 1. ("Kimi K3 is here: efficient day-0 support on vLLM", summary:
+ * fused kernels for KDA decode.)                                                           */
+kda_status kda_decode(kda_pool* pool, const kda_step_args* args, void* stream);
+
+/* Speculative verify of n_pos = 1 + T positions (1 <= n_pos <= ring_cap): steps a register
+ * copy of the committed state through the positions, writes o for each, and appends each
+ * position's (k, v, a, b) to the slot's ring from ring_head on (mod ring_cap). The committed
+ * state is NOT written. Marks the slot pending (v_base = ring_head, v_npos = pending = n_pos).
+ * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "ReplaySSM shrinks rollback state":
+ * recent inputs stay in a buffer, the accepted state is rebuilt at commit.)                */
+kda_status kda_verify(kda_pool* pool, const kda_step_args* args, int32_t n_pos, void* stream);
+
+/* ReplaySSM commit. d_n_accepted[B] (device, e.g. written by an on-GPU sampler) gives the
+ * accepted drafts n per sequence; 1 + n ring entries from v_base are replayed into the slot
+ * with the same arithmetic as kda_decode (bit-identical to 1 + n decode calls), the state
+ * is written once, ring_head = (v_base + 1 + n) mod ring_cap, pos += 1 + n, pending = 0.
+ * n outside [0, v_npos - 1] sets KDA_DEVERR_NACC_RANGE and is clamped. Slots must be pending. */
+kda_status kda_commit(kda_pool* pool, int32_t B, const int32_t* h_slots,
+                      const int32_t* d_slots, const int32_t* d_n_accepted, void* stream);
+
+/* Reject every drafted position: only pending is cleared; state, ring_head and pos keep
+ * their values ("ReplaySSM shrinks rollback state": a reject only moves the buffer pointer). */
+kda_status kda_rollback(kda_pool* pool, int32_t B, const int32_t* h_slots,
+                        const int32_t* d_slots, void* stream);
+
+/* ---- mixed speculative / non-speculative batch ---------------------------------------
+ * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "Small tensor copies leave the hot
+ * path": contiguous zero-copy slices and direct output writes instead of index_select /
+ * index_copy.) One packed token buffer [prefill tokens | decode tokens | verify tokens]:
+ * prefill sequences take the first prefill.n_tok rows (cu_seqlens relative to row 0),
+ * n_decode decode tokens follow, then n_verify * n_pos verify tokens ([seq][pos] order).
+ * o is written in the same packing. The three parts run on `stream` in that order with no
+ * gather or scatter; the prefill's token pointers and the step slot arrays of `prefill`,
+ * `decode` and `verify` are ignored in favour of the packed ones below.                  */
+typedef struct {
+  const void* q; const void* k; const void* v;   /* bf16 [n_total][H][d] */
+  const float* a; const float* b;
+  void* o;                                       /* bf16 [n_total][H][dv] */
+  kda_prefill_args prefill;                      /* slot arrays, seqlens, chunk, interval */
+  int32_t n_decode;
+  const int32_t* h_decode_slots; const int32_t* d_decode_slots;
+  int32_t n_verify, n_pos;
+  const int32_t* h_verify_slots; const int32_t* d_verify_slots;
+} kda_mixed_args;
+kda_status kda_mixed_batch(kda_pool* pool, const kda_mixed_args* args, void* stream);
+
+/* ---- errors ------------------------------------------------------------------------- */
+/* Synchronises `stream`, returns the device error word in *bits_out and clears it.       */
+kda_status kda_read_device_error(kda_pool* pool, uint32_t* bits_out, void* stream);
+const char* kda_status_string(kda_status status);
+const char* kda_last_error(void);
+
+/* Host-side view of a slot: 0 free, 1 idle, 2 pending; -1 for an id out of range.          */
+int32_t kda_slot_host_state(const kda_pool* pool, int32_t slot);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

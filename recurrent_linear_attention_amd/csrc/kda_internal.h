@@ -1,0 +1,59 @@
+// Internal interface between the host-side pool logic (kda_pool.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Device-side view of a pool: raw pointers and geometry, passed by value to launchers.
+struct PoolView {
+  float* state;             // [num_slots][H][dk][dv]
+  uint16_t* ring_k;         // bf16 [num_slots][R][H][dk]
+  uint16_t* ring_v;         // bf16 [num_slots][R][H][dv]
+  float* ring_a;            // [num_slots][R][H][dk]
+  float* ring_b;            // [num_slots][R][H]
+  kda_slot_meta* meta;      // [num_slots]
+  uint32_t* err;            // device error word
+  int32_t num_slots, H, dk, dv, R;
+};
+
+struct StepTensors {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v;   // bf16 bits
+  const float* a; const float* b;
+  uint16_t* o;
+};
+
+struct PrefillLaunch {
+  StepTensors t;
+  int32_t n_seq, n_tok, chunk, ckpt_interval;
+  const int32_t* cu_seqlens;   // device
+  const int32_t* init_slot;    // device or nullptr
+  const int32_t* out_slot;     // device
+  const int32_t* ckpt_slot;    // device or nullptr
+  int32_t max_len;             // longest sequence (host-known), sizes the grid
+};
+
+hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B,
+                         const int32_t* d_slots, hipStream_t s);
+hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
+                         const int32_t* d_slots, hipStream_t s);
+hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots,
+                         const int32_t* d_n_accepted, hipStream_t s);
+hipError_t launch_rollback(const PoolView& p, int32_t B, const int32_t* d_slots,
+                           hipStream_t s);
+hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s);
+hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s);
+hipError_t launch_clear_word(uint32_t* w, hipStream_t s);
+hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
+// Token-by-token prefill with the decode step (reference-form kernel; any supported d).
+hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
+
+// Shapes the kernels are instantiated for.
+inline bool supported_dim(int d) { return d == 16 || d == 128; }
+inline int prefill_chunk_for(int d) { return d == 16 ? 16 : 64; }
+
+}  // namespace kda

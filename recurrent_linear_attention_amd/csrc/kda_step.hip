@@ -1,0 +1,441 @@
+// KDA single-token kernels on gfx950: decode, speculative verify, ReplaySSM commit and
+// rollback, plus the slot reset / checkpoint copies.
+//
+// The token update is the gated delta rule with per-key-channel decay (the pages name the
+// KDA state -- "vLLM lifts Kimi K3 throughput by up to 2.8x", section "Kimi K3 stresses the
+// whole stack" -- but print no formula):
+//     S' = Diag(a) S;  u = S'^T k;  p = S'^T q;  delta = b (v - u)
+//     S  = S' + k delta^T;  o = S^T q = p + (k . q) delta
+// These kernels are HBM-bound (about 0.9 flop per byte): each (sequence, head, value-column
+// slice) work-group streams its fp32 state tile in once with 16-byte loads, keeps it in
+// VGPRs for every position it processes, and writes it back at most once.
+//
+// Thread layout (StepCfg): a work-group owns VS value columns of one head. Thread t holds
+// RPT consecutive key rows x 4 consecutive columns (one float4 per row). The reductions over
+// key rows (u, p and k.q) go first through the thread's own rows, then a butterfly across
+// the lanes of a wave that hold the same columns, then across waves through LDS in wave
+// order. Decode, verify and commit use the same layout and the same step function, so a
+// commit that replays n positions yields the state bit-for-bit equal to n decode calls.
+#include <hip/hip_runtime.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+template <int D>
+struct StepCfg;
+
+template <>
+struct StepCfg<128> {
+  static constexpr int D = 128, VS = 32, RPT = 8;
+  static constexpr int TPR = VS / 4, NRG = D / RPT, NT = NRG * TPR, NW = NT / 64;
+};
+
+template <>
+struct StepCfg<16> {
+  static constexpr int D = 16, VS = 16, RPT = 1;
+  static constexpr int TPR = VS / 4, NRG = D / RPT, NT = NRG * TPR, NW = NT / 64;
+};
+
+template <class C>
+struct StepIn {
+  uint32_t kw[(C::RPT + 1) / 2];   // raw bf16 of k rows
+  uint32_t vw[2];                  // raw bf16 of the thread's 4 value columns
+  float k[C::RPT], q[C::RPT], a[C::RPT], v[4];
+  float b;
+};
+
+// Cross-wave reduction scratch: two buffers so one barrier per step suffices.
+template <class C>
+struct StepLds {
+  float red[2][C::NW][2 * C::VS + 4];
+};
+
+template <class C>
+__device__ __forceinline__ float rows_sum(float x) {
+#pragma unroll
+  for (int m = C::TPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One position of the rule on the thread's RPT x 4 tile. WITH_O also produces o for the
+// thread's 4 columns (valid in every thread).
+template <class C, bool WITH_O>
+__device__ __forceinline__ void step(float (&S)[C::RPT][4], const StepIn<C>& in,
+                                     StepLds<C>& lds, int buf, float (&o)[4]) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, cg = t % C::TPR;
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[r][c] = S[r][c] * in.a[r];
+  float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u[c] = __builtin_fmaf(S[r][c], in.k[r], u[c]);
+      if constexpr (WITH_O) p[c] = __builtin_fmaf(S[r][c], in.q[r], p[c]);
+    }
+  if constexpr (WITH_O) {
+#pragma unroll
+    for (int r = 0; r < C::RPT; ++r) kq = __builtin_fmaf(in.k[r], in.q[r], kq);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u[c] = rows_sum<C>(u[c]);
+    if constexpr (WITH_O) p[c] = rows_sum<C>(p[c]);
+  }
+  if constexpr (WITH_O) kq = rows_sum<C>(kq);
+  if constexpr (C::NW > 1) {
+    float* red = lds.red[buf][w];
+    if (lane < C::TPR) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        red[cg * 4 + c] = u[c];
+        if constexpr (WITH_O) red[C::VS + cg * 4 + c] = p[c];
+      }
+      if (WITH_O && lane == 0) red[2 * C::VS] = kq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u[c] = lds.red[buf][0][cg * 4 + c];
+      if constexpr (WITH_O) p[c] = lds.red[buf][0][C::VS + cg * 4 + c];
+    }
+    if constexpr (WITH_O) kq = lds.red[buf][0][2 * C::VS];
+#pragma unroll
+    for (int ww = 1; ww < C::NW; ++ww) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u[c] = u[c] + lds.red[buf][ww][cg * 4 + c];
+        if constexpr (WITH_O) p[c] = p[c] + lds.red[buf][ww][C::VS + cg * 4 + c];
+      }
+      if constexpr (WITH_O) kq = kq + lds.red[buf][ww][2 * C::VS];
+    }
+  }
+  float dl[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) dl[c] = in.b * (in.v[c] - u[c]);
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[r][c] = __builtin_fmaf(in.k[r], dl[c], S[r][c]);
+  if constexpr (WITH_O) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = __builtin_fmaf(kq, dl[c], p[c]);
+  }
+}
+
+// Inputs of one position: k, a (and q) rows r0..r0+RPT-1 and v columns c0..c0+3.
+template <class C, bool WITH_Q>
+__device__ __forceinline__ void load_in(StepIn<C>& in, const uint16_t* q, const uint16_t* k,
+                                        const uint16_t* v, const float* a, const float* b,
+                                        int r0, int c0) {
+  load_bf16_raw<C::RPT>(k + r0, in.kw);
+  unpack_bf16<C::RPT>(in.kw, in.k);
+  if constexpr (WITH_Q) {
+    uint32_t qw[(C::RPT + 1) / 2];
+    load_bf16_raw<C::RPT>(q + r0, qw);
+    unpack_bf16<C::RPT>(qw, in.q);
+  }
+  load_f32<C::RPT>(a + r0, in.a);
+  load_bf16_raw<4>(v + c0, in.vw);
+  unpack_bf16<4>(in.vw, in.v);
+  in.b = *b;
+}
+
+template <class C>
+__device__ __forceinline__ void load_state(float (&S)[C::RPT][4], const float* Sp, int r0, int c0) {
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r) {
+    float4 x = *reinterpret_cast<const float4*>(Sp + (size_t)(r0 + r) * C::D + c0);
+    S[r][0] = x.x; S[r][1] = x.y; S[r][2] = x.z; S[r][3] = x.w;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_state(const float (&S)[C::RPT][4], float* Sp, int r0, int c0) {
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r)
+    *reinterpret_cast<float4*>(Sp + (size_t)(r0 + r) * C::D + c0) =
+        make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+}
+
+__device__ __forceinline__ int wrap(int x, int R) { return ((x % R) + R) % R; }
+
+// grid: B * H * (D / VS); block (bi, h, vs) with vs fastest.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void decode_kernel(PoolView P, StepTensors T,
+                                                                const int32_t* __restrict__ slots) {
+  using C = StepCfg<D>;
+  __shared__ StepLds<C> lds;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
+  float S[C::RPT][4];
+  load_state<C>(S, Sp, r0, c0);
+  const size_t row = (size_t)bi * P.H + h;
+  StepIn<C> in;
+  load_in<C, true>(in, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+  float o[4];
+  step<C, true>(S, in, lds, 0, o);
+  store_state<C>(S, Sp, r0, c0);
+  if (rg == 0) {
+    uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+    store_bf16_raw<4>(T.o + row * D + c0, ow);
+  }
+  if (t == 0 && h == 0 && vs == 0) P.meta[slot].pos += 1;
+}
+
+// Speculative verify: n_pos positions on a register copy; outputs + ring appends only.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, StepTensors T, int n_pos,
+                                                                const int32_t* __restrict__ slots) {
+  using C = StepCfg<D>;
+  __shared__ StepLds<C> lds;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  const int R = P.R;
+  const int head = wrap(P.meta[slot].ring_head, R);
+  const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
+  float S[C::RPT][4];
+  load_state<C>(S, Sp, r0, c0);
+  for (int j = 0; j < n_pos; ++j) {
+    const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
+    StepIn<C> in;
+    load_in<C, true>(in, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+    float o[4];
+    step<C, true>(S, in, lds, j & 1, o);
+    const size_t e = ((size_t)slot * R + (size_t)wrap(head + j, R)) * P.H + h;
+    if (rg == 0) {
+      uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+      store_bf16_raw<4>(T.o + row * D + c0, ow);
+      store_bf16_raw<4>(P.ring_v + e * D + c0, in.vw);
+    }
+    if (vs == 0 && cg == 0) {
+      store_bf16_raw<C::RPT>(P.ring_k + e * D + r0, in.kw);
+      store_f32<C::RPT>(P.ring_a + e * D + r0, in.a);
+      if (t == 0) P.ring_b[e] = in.b;
+    }
+  }
+  if (t == 0 && h == 0 && vs == 0) {
+    P.meta[slot].v_base = head;
+    P.meta[slot].v_npos = n_pos;
+    P.meta[slot].pending = n_pos;
+  }
+}
+
+// ReplaySSM commit: replay 1 + n_accepted ring entries into the slot, store once.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, const int32_t* __restrict__ slots,
+                                                                const int32_t* __restrict__ n_acc) {
+  using C = StepCfg<D>;
+  __shared__ StepLds<C> lds;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  const int R = P.R;
+  const int vb = wrap(P.meta[slot].v_base, R);
+  int vn = P.meta[slot].v_npos;
+  vn = vn < 1 ? 1 : (vn > R ? R : vn);
+  int na = n_acc[bi];
+  const bool bad = na < 0 || na > vn - 1;
+  na = na < 0 ? 0 : (na > vn - 1 ? vn - 1 : na);
+  const int n = 1 + na;
+  float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
+  float S[C::RPT][4];
+  load_state<C>(S, Sp, r0, c0);
+  for (int j = 0; j < n; ++j) {
+    const size_t e = ((size_t)slot * R + (size_t)wrap(vb + j, R)) * P.H + h;
+    StepIn<C> in;
+    load_in<C, false>(in, nullptr, P.ring_k + e * D, P.ring_v + e * D, P.ring_a + e * D,
+                      P.ring_b + e, r0, c0);
+    float o[4];
+    step<C, false>(S, in, lds, j & 1, o);
+  }
+  store_state<C>(S, Sp, r0, c0);
+  if (t == 0 && h == 0 && vs == 0) {
+    P.meta[slot].ring_head = wrap(vb + n, R);
+    P.meta[slot].pos += n;
+    P.meta[slot].pending = 0;
+    if (bad) atomicOr(P.err, (uint32_t)KDA_DEVERR_NACC_RANGE);
+  }
+}
+
+// Recurrent-form prefill: one work-group per (sequence, head, value slice) walks its
+// sequence token by token with the decode step, exporting the state at every checkpoint
+// boundary inside the same pass and the final state at the end.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void prefill_recurrent_kernel(PoolView P, PrefillLaunch A) {
+  using C = StepCfg<D>;
+  __shared__ StepLds<C> lds;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, si = blockIdx.x / (NVS * P.H);
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  const int lo = A.cu_seqlens[si], hi = A.cu_seqlens[si + 1];
+  int ck = 0;   // first checkpoint entry of this sequence
+  if (A.ckpt_interval > 0)
+    for (int j = 0; j < si; ++j) ck += (A.cu_seqlens[j + 1] - A.cu_seqlens[j]) / A.ckpt_interval;
+  const int init = A.init_slot ? A.init_slot[si] : -1;
+  const int out = A.out_slot[si];
+  const size_t per = (size_t)P.H * D * D, hoff = (size_t)h * D * D;
+  float S[C::RPT][4];
+  if (init >= 0 && init < P.num_slots) {
+    load_state<C>(S, P.state + init * per + hoff, r0, c0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < C::RPT; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[r][c] = 0.f;
+  }
+  const int64_t pos0 = (init >= 0 && init < P.num_slots) ? P.meta[init].pos : 0;
+  for (int tok = lo; tok < hi; ++tok) {
+    const size_t row = (size_t)tok * P.H + h;
+    StepIn<C> in;
+    load_in<C, true>(in, A.t.q + row * D, A.t.k + row * D, A.t.v + row * D, A.t.a + row * D,
+                     A.t.b + row, r0, c0);
+    float o[4];
+    step<C, true>(S, in, lds, tok & 1, o);
+    if (rg == 0) {
+      uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+      store_bf16_raw<4>(A.t.o + row * D + c0, ow);
+    }
+    const int done = tok + 1 - lo;
+    if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
+      const int dst = A.ckpt_slot[ck++];
+      if (dst >= 0 && dst < P.num_slots) {
+        store_state<C>(S, P.state + dst * per + hoff, r0, c0);
+        if (t == 0 && h == 0 && vs == 0) {
+          kda_slot_meta m{pos0 + done, 0, 0, 0, 0};
+          P.meta[dst] = m;
+        }
+      }
+    }
+  }
+  if (out >= 0 && out < P.num_slots) {
+    store_state<C>(S, P.state + out * per + hoff, r0, c0);
+    if (t == 0 && h == 0 && vs == 0) {
+      kda_slot_meta m{pos0 + (hi - lo), 0, 0, 0, 0};
+      P.meta[out] = m;
+    }
+  }
+}
+
+__global__ void rollback_kernel(PoolView P, int B, const int32_t* __restrict__ slots) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B) return;
+  const int slot = slots[i];
+  if (slot < 0 || slot >= P.num_slots) {
+    atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  P.meta[slot].pending = 0;
+}
+
+// Zero (src < 0) or copy one slot's state; block 0 thread 0 also writes dst's metadata.
+__global__ void slot_fill_kernel(PoolView P, int src, int dst, size_t n4) {
+  const size_t per = (size_t)P.H * P.dk * P.dv;
+  float4* d = reinterpret_cast<float4*>(P.state + (size_t)dst * per);
+  const float4* s = src >= 0 ? reinterpret_cast<const float4*>(P.state + (size_t)src * per) : nullptr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
+    d[i] = s ? s[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    kda_slot_meta m;
+    m.pos = src >= 0 ? P.meta[src].pos : 0;
+    m.ring_head = 0; m.pending = 0; m.v_base = 0; m.v_npos = 0;
+    P.meta[dst] = m;
+  }
+}
+
+__global__ void clear_word_kernel(uint32_t* w) { *w = 0u; }
+
+template <int D>
+int step_blocks(const PoolView& p, int B) { return B * p.H * (D / StepCfg<D>::VS); }
+
+}  // namespace
+
+hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, const int32_t* d_slots,
+                         hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(decode_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, t, d_slots);
+  else
+    hipLaunchKernelGGL(decode_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, t, d_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
+                         const int32_t* d_slots, hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(verify_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, t, n_pos, d_slots);
+  else
+    hipLaunchKernelGGL(verify_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, t, n_pos, d_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots, const int32_t* d_n_acc,
+                         hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(commit_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, d_slots, d_n_acc);
+  else
+    hipLaunchKernelGGL(commit_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, d_slots, d_n_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(prefill_recurrent_kernel<128>, dim3(a.n_seq * p.H * (128 / StepCfg<128>::VS)),
+                       dim3(StepCfg<128>::NT), 0, s, p, a);
+  else
+    hipLaunchKernelGGL(prefill_recurrent_kernel<16>, dim3(a.n_seq * p.H * (16 / StepCfg<16>::VS)),
+                       dim3(StepCfg<16>::NT), 0, s, p, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rollback(const PoolView& p, int32_t B, const int32_t* d_slots, hipStream_t s) {
+  hipLaunchKernelGGL(rollback_kernel, dim3((B + 63) / 64), dim3(64), 0, s, p, B, d_slots);
+  return hipGetLastError();
+}
+
+static hipError_t launch_fill(const PoolView& p, int src, int dst, hipStream_t s) {
+  const size_t n4 = (size_t)p.H * p.dk * p.dv / 4;
+  int blocks = (int)((n4 + 255) / 256);
+  blocks = blocks > 1024 ? 1024 : blocks;
+  hipLaunchKernelGGL(slot_fill_kernel, dim3(blocks), dim3(256), 0, s, p, src, dst, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s) { return launch_fill(p, -1, slot, s); }
+
+hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s) {
+  return launch_fill(p, src, dst, s);
+}
+
+hipError_t launch_clear_word(uint32_t* w, hipStream_t s) {
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, s, w);
+  return hipGetLastError();
+}
+
+}  // namespace kda

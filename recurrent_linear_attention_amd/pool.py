@@ -1,0 +1,236 @@
+"""Python binding of the KDA C ABI: the same entry points, taking torch tensors.
+
+Argument marshalling only -- torch provides device memory and the current HIP stream, the
+library (``lib/libkda.so``) does all the work. Index arrays given as plain sequences are
+copied to the device on torch's current stream, so calls should run on that stream. ``KDAPool`` owns the three caller-side device
+buffers (state, ReplaySSM ring, metadata) and the library's pool handle.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_size_t, c_uint32, c_void_p
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import check, lib
+
+__all__ = ["KDAPool", "IndexArray", "chunk_for"]
+
+
+def chunk_for(d: int) -> int:
+    """The prefill chunk this build instantiates for head dim d."""
+    return 16 if d == 16 else 64
+
+
+def _stream(stream=None) -> c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor | None, dtype, name: str) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ix(values, device) -> "IndexArray":
+    return values if isinstance(values, IndexArray) else IndexArray(values, device)
+
+
+class IndexArray:
+    """An int32 index array held twice, as the ABI wants it: a host copy (validation and
+    bookkeeping) and a device copy (read by the kernels). Build once and reuse it to keep
+    host-to-device copies out of a timed loop."""
+
+    def __init__(self, values, device):
+        self.np = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
+        self.dev = torch.from_numpy(self.np).to(device, non_blocking=False)
+
+    @property
+    def h(self):
+        return self.np.ctypes.data if self.np.size else None
+
+    @property
+    def d(self):
+        return self.dev.data_ptr() if self.np.size else None
+
+
+class KDAPool:
+    """A pool of fp32 KDA state slots with per-slot ReplaySSM rings, on one GPU."""
+
+    def __init__(self, num_slots: int, num_heads: int, d: int, ring_cap: int = 9,
+                 device: str | torch.device = "cuda"):
+        self.device = torch.device(device)
+        self.desc = _abi.kda_pool_desc(num_slots, num_heads, d, d, ring_cap)
+        self.num_slots, self.H, self.d, self.R = num_slots, num_heads, d, ring_cap
+        sb = lib.kda_state_bytes(byref(self.desc))
+        if sb == 0:
+            raise ValueError(f"unsupported pool geometry (d={d})")
+        self.state = torch.zeros((num_slots, num_heads, d, d), dtype=torch.float32,
+                                 device=self.device)
+        self.ring = torch.zeros(lib.kda_ring_bytes(byref(self.desc)), dtype=torch.uint8,
+                                device=self.device)
+        self.meta = torch.zeros(lib.kda_meta_bytes(byref(self.desc)), dtype=torch.uint8,
+                                device=self.device)
+        h = c_void_p()
+        check(lib.kda_pool_create(byref(self.desc), self.state.data_ptr(), self.ring.data_ptr(),
+                                  self.meta.data_ptr(), byref(h)), "kda_pool_create")
+        self.handle = h
+        off = (c_size_t * 4)()
+        check(lib.kda_ring_layout(byref(self.desc), off), "kda_ring_layout")
+        self.ring_offsets = list(off)
+        self.err_offset = lib.kda_meta_error_offset(byref(self.desc))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib.kda_pool_destroy(h)
+            self.handle = None
+
+    # ------------------------------------------------------------------ slots
+    def kda_slot_alloc(self) -> int:
+        s = c_int32()
+        check(lib.kda_slot_alloc(self.handle, byref(s)), "kda_slot_alloc")
+        return s.value
+
+    def kda_slot_free(self, slot: int) -> None:
+        check(lib.kda_slot_free(self.handle, slot), "kda_slot_free")
+
+    def kda_slot_reset(self, slot: int, stream=None) -> None:
+        check(lib.kda_slot_reset(self.handle, slot, _stream(stream)), "kda_slot_reset")
+
+    def kda_slot_checkpoint(self, src: int, dst: int, stream=None) -> None:
+        check(lib.kda_slot_checkpoint(self.handle, src, dst, _stream(stream)),
+              "kda_slot_checkpoint")
+
+    def host_state(self, slot: int) -> int:
+        return lib.kda_slot_host_state(self.handle, slot)
+
+    # ------------------------------------------------------------------ helpers
+    def _tok_ptrs(self, q, k, v, a, b, o):
+        return (_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+                _dev(v, torch.bfloat16, "v"), _dev(a, torch.float32, "a"),
+                _dev(b, torch.float32, "b"), _dev(o, torch.bfloat16, "o"))
+
+    def _prefill_struct(self, n_tok, cu, init, out, ckpt, chunk, interval, ptrs):
+        args = _abi.kda_prefill_args(*ptrs)
+        args.n_seq = cu.np.size - 1
+        args.n_tok = n_tok
+        args.chunk = chunk
+        args.ckpt_interval = interval
+        args.h_cu_seqlens, args.d_cu_seqlens = cu.h, cu.d
+        if init is not None:
+            args.h_init_slot, args.d_init_slot = init.h, init.d
+        args.h_out_slot, args.d_out_slot = out.h, out.d
+        if ckpt is not None:
+            args.h_ckpt_slot, args.d_ckpt_slot = ckpt.h, ckpt.d
+        return args
+
+    # ------------------------------------------------------------------ the three uses
+    def kda_prefill(self, q, k, v, a, b, cu_seqlens, out_slots, init_slots=None,
+                    ckpt_slots=None, ckpt_interval: int = 0, chunk: int | None = None,
+                    o=None, stream=None) -> torch.Tensor:
+        """Packed varlen prefill; q, k, a [N, H, d], v [N, H, d], b [N, H]. Returns o."""
+        n_tok = q.shape[0]
+        if o is None:
+            o = torch.empty((n_tok, self.H, self.d), dtype=torch.bfloat16, device=q.device)
+        cu = _ix(cu_seqlens, self.device)
+        out = _ix(out_slots, self.device)
+        init = None if init_slots is None else _ix(init_slots, self.device)
+        ckpt = None if ckpt_slots is None or len(ckpt_slots) == 0 else _ix(ckpt_slots, self.device)
+        args = self._prefill_struct(n_tok, cu, init, out, ckpt,
+                                    chunk or chunk_for(self.d), ckpt_interval,
+                                    self._tok_ptrs(q, k, v, a, b, o))
+        check(lib.kda_prefill(self.handle, byref(args), _stream(stream)), "kda_prefill")
+        return o
+
+    def _step_args(self, q, k, v, a, b, o, slots):
+        s = _ix(slots, self.device)
+        args = _abi.kda_step_args(*self._tok_ptrs(q, k, v, a, b, o))
+        args.B = s.np.size
+        args.h_slots, args.d_slots = s.h, s.d
+        return args, s
+
+    def kda_decode(self, q, k, v, a, b, slots, o=None, stream=None) -> torch.Tensor:
+        """One token per sequence: q, k, a, v [B, H, d], b [B, H]. Returns o [B, H, d]."""
+        if o is None:
+            o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
+        args, keep = self._step_args(q, k, v, a, b, o, slots)
+        check(lib.kda_decode(self.handle, byref(args), _stream(stream)), "kda_decode")
+        return o
+
+    def kda_verify(self, q, k, v, a, b, slots, o=None, stream=None) -> torch.Tensor:
+        """Verify P positions per sequence: q, k, a, v [B, P, H, d], b [B, P, H]."""
+        n_pos = q.shape[1]
+        if o is None:
+            o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
+        args, keep = self._step_args(q, k, v, a, b, o, slots)
+        check(lib.kda_verify(self.handle, byref(args), n_pos, _stream(stream)), "kda_verify")
+        return o
+
+    def kda_commit(self, slots, n_accepted: torch.Tensor, stream=None) -> None:
+        """n_accepted: device int32 [B] (accepted drafts per sequence)."""
+        s = _ix(slots, self.device)
+        na = _dev(n_accepted, torch.int32, "n_accepted")
+        check(lib.kda_commit(self.handle, s.np.size, s.h, s.d, na, _stream(stream)),
+              "kda_commit")
+
+    def kda_rollback(self, slots, stream=None) -> None:
+        s = _ix(slots, self.device)
+        check(lib.kda_rollback(self.handle, s.np.size, s.h, s.d, _stream(stream)),
+              "kda_rollback")
+
+    def kda_mixed_batch(self, q, k, v, a, b, cu_seqlens, out_slots, decode_slots,
+                        verify_slots, n_pos: int, init_slots=None, ckpt_slots=None,
+                        ckpt_interval: int = 0, o=None, stream=None) -> torch.Tensor:
+        """One packed batch [prefill tokens | decode tokens | verify tokens ([seq][pos])]."""
+        if o is None:
+            o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
+        ptrs = self._tok_ptrs(q, k, v, a, b, o)
+        cu = _ix(cu_seqlens, self.device)
+        out = _ix(out_slots, self.device)
+        init = None if init_slots is None else _ix(init_slots, self.device)
+        ckpt = None if ckpt_slots is None or len(ckpt_slots) == 0 else _ix(ckpt_slots, self.device)
+        dec = _ix(decode_slots, self.device)
+        ver = _ix(verify_slots, self.device)
+        m = _abi.kda_mixed_args(*ptrs)
+        m.prefill = self._prefill_struct(int(cu.np[-1]), cu, init, out, ckpt, chunk_for(self.d),
+                                         ckpt_interval, (None,) * 6)
+        m.n_decode, m.h_decode_slots, m.d_decode_slots = dec.np.size, dec.h, dec.d
+        m.n_verify, m.n_pos = ver.np.size, n_pos
+        m.h_verify_slots, m.d_verify_slots = ver.h, ver.d
+        check(lib.kda_mixed_batch(self.handle, byref(m), _stream(stream)), "kda_mixed_batch")
+        return o
+
+    def kda_read_device_error(self, stream=None) -> int:
+        bits = c_uint32()
+        check(lib.kda_read_device_error(self.handle, byref(bits), _stream(stream)),
+              "kda_read_device_error")
+        return bits.value
+
+    # ------------------------------------------------------------------ views for checks
+    def meta_array(self) -> np.ndarray:
+        """[num_slots, 5] int64: pos, ring_head, pending, v_base, v_npos (synchronous copy)."""
+        raw = self.meta[: self.num_slots * 24].cpu().numpy()
+        rec = raw.view(np.dtype([("pos", "<i8"), ("ring_head", "<i4"), ("pending", "<i4"),
+                                 ("v_base", "<i4"), ("v_npos", "<i4")]))
+        return np.stack([rec[f].astype(np.int64) for f in rec.dtype.names], axis=1)
+
+    def ring_tensors(self):
+        """Views of the ring sections: k, v bf16 [S, R, H, d]; a fp32 [S, R, H, d]; b [S, R, H]."""
+        S, R, H, d = self.num_slots, self.R, self.H, self.d
+        n = S * R * H
+        o = self.ring_offsets
+        k = self.ring[o[0]:o[0] + n * d * 2].view(torch.bfloat16).view(S, R, H, d)
+        v = self.ring[o[1]:o[1] + n * d * 2].view(torch.bfloat16).view(S, R, H, d)
+        a = self.ring[o[2]:o[2] + n * d * 4].view(torch.float32).view(S, R, H, d)
+        b = self.ring[o[3]:o[3] + n * 4].view(torch.float32).view(S, R, H)
+        return k, v, a, b

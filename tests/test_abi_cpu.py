@@ -1,0 +1,201 @@
+"""CPU-side checks of the C ABI: the library loads and exports every declared symbol, the
+size helpers follow the documented layouts, and the host-side pool bookkeeping and argument
+validation behave as documented. No call here reaches a kernel launch: pools are created
+over placeholder device addresses, and every exercised path fails validation first or is
+host-only."""
+import ctypes
+import os
+import re
+from ctypes import byref, c_int32, c_size_t, c_void_p
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "recurrent_linear_attention_amd", "lib", "libkda.so")
+if not os.path.exists(LIB):   # the library is built, not committed
+    from recurrent_linear_attention_amd import build as _b
+    _b.build()
+
+from recurrent_linear_attention_amd import _abi  # noqa: E402
+from recurrent_linear_attention_amd._abi import lib  # noqa: E402
+from oracle import KDAPool as OraclePool  # noqa: E402
+
+FAKE = 1 << 20          # 256-aligned placeholder "device" address, never dereferenced
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(kda_\w+)\s*\(", src))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(_abi.PROTOTYPES), names ^ set(_abi.PROTOTYPES)
+
+
+def desc(n=8, H=2, d=16, R=9):
+    return _abi.kda_pool_desc(n, H, d, d, R)
+
+
+def test_size_helpers():
+    d = desc(n=256, H=32, d=128, R=9)
+    assert lib.kda_state_bytes(byref(d)) == 256 * 32 * 128 * 128 * 4
+    off = (c_size_t * 4)()
+    assert lib.kda_ring_layout(byref(d), off) == 0
+    per = 256 * 9 * 32
+    assert off[0] == 0 and off[1] >= per * 128 * 2 and off[2] >= off[1] + per * 128 * 2
+    assert off[3] >= off[2] + per * 128 * 4 and all(o % 256 == 0 for o in off)
+    assert lib.kda_ring_bytes(byref(d)) >= off[3] + per * 4
+    assert lib.kda_meta_error_offset(byref(d)) >= 256 * 24
+    assert lib.kda_meta_bytes(byref(d)) >= lib.kda_meta_error_offset(byref(d)) + 4
+    assert ctypes.sizeof(_abi.kda_slot_meta) == 24
+    bad = _abi.kda_pool_desc(8, 2, 64, 64, 9)
+    assert lib.kda_state_bytes(byref(bad)) == 0          # d = 64 not instantiated
+
+
+class HostPool:
+    def __init__(self, n=8, H=2, d=16, R=9):
+        self.d = desc(n, H, d, R)
+        h = c_void_p()
+        assert lib.kda_pool_create(byref(self.d), FAKE, FAKE, FAKE, byref(h)) == 0
+        self.h = h
+
+    def __del__(self):
+        lib.kda_pool_destroy(self.h)
+
+    def alloc(self):
+        s = c_int32()
+        st = lib.kda_slot_alloc(self.h, byref(s))
+        return st, s.value
+
+
+def test_pool_create_rejects_bad_arguments():
+    h = c_void_p()
+    d = desc()
+    assert lib.kda_pool_create(byref(d), None, FAKE, FAKE, byref(h)) == _abi.KDA_EINVAL
+    assert lib.kda_pool_create(byref(d), FAKE + 4, FAKE, FAKE, byref(h)) == _abi.KDA_EINVAL
+    d64 = _abi.kda_pool_desc(8, 2, 64, 64, 9)
+    assert lib.kda_pool_create(byref(d64), FAKE, FAKE, FAKE, byref(h)) == _abi.KDA_EUNSUPPORTED
+    d0 = _abi.kda_pool_desc(8, 2, 16, 16, 0)
+    assert lib.kda_pool_create(byref(d0), FAKE, FAKE, FAKE, byref(h)) == _abi.KDA_EINVAL
+    assert b"ring_cap" in lib.kda_last_error()
+
+
+def test_alloc_free_trace_matches_oracle_model():
+    rng = np.random.default_rng(0)
+    p, m = HostPool(n=16), OraclePool(16, 1, 2, 2, 3)
+    for _ in range(400):
+        if rng.random() < 0.55:
+            st, s = p.alloc()
+            try:
+                ms = m.alloc()
+                assert st == 0 and s == ms
+            except LookupError:
+                assert st == _abi.KDA_ENOSLOT
+        else:
+            s = int(rng.integers(-1, 17))
+            st = lib.kda_slot_free(p.h, s)
+            try:
+                m.free(s)
+                assert st == 0
+            except (ValueError, IndexError):
+                assert st == _abi.KDA_EINVAL
+        for s in range(16):
+            assert lib.kda_slot_host_state(p.h, s) == int(m.live[s])
+
+
+def i32(*v):
+    return np.array(v, dtype=np.int32)
+
+
+def step_args(B, slots):
+    a = _abi.kda_step_args(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    a.B = B
+    a.h_slots = slots.ctypes.data
+    a.d_slots = FAKE
+    return a
+
+
+def test_step_validation_errors_launch_nothing():
+    p = HostPool()
+    s0, s1 = p.alloc()[1], p.alloc()[1]
+    dead = i32(5)
+    assert lib.kda_decode(p.h, byref(step_args(1, dead)), None) == _abi.KDA_EINVAL
+    dup = i32(s0, s0)
+    assert lib.kda_decode(p.h, byref(step_args(2, dup)), None) == _abi.KDA_EINVAL
+    assert b"repeats" in lib.kda_last_error()
+    ok = i32(s0, s1)
+    assert lib.kda_verify(p.h, byref(step_args(2, ok)), 10, None) == _abi.KDA_EINVAL
+    assert lib.kda_verify(p.h, byref(step_args(2, ok)), 0, None) == _abi.KDA_EINVAL
+    # commit / rollback of idle slots: wrong state
+    assert lib.kda_commit(p.h, 2, ok.ctypes.data, FAKE, FAKE, None) == _abi.KDA_ESTATE
+    assert lib.kda_rollback(p.h, 2, ok.ctypes.data, FAKE, None) == _abi.KDA_ESTATE
+    # misaligned token tensor
+    a = step_args(2, ok)
+    a.q = FAKE + 2
+    assert lib.kda_decode(p.h, byref(a), None) == _abi.KDA_EINVAL
+    # nothing changed host-side
+    assert lib.kda_slot_host_state(p.h, s0) == 1 and lib.kda_slot_host_state(p.h, s1) == 1
+    # zero-size batches are no-ops
+    assert lib.kda_decode(p.h, byref(step_args(0, ok)), None) == 0
+    assert lib.kda_slot_reset(p.h, 7, None) == _abi.KDA_EINVAL
+    assert lib.kda_slot_checkpoint(p.h, s0, s0, None) == _abi.KDA_EINVAL
+
+
+def prefill_args(cu, out, init=None, ckpt=None, chunk=16, interval=0):
+    a = _abi.kda_prefill_args(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    a.n_seq, a.n_tok, a.chunk, a.ckpt_interval = cu.size - 1, int(cu[-1]), chunk, interval
+    a.h_cu_seqlens, a.d_cu_seqlens = cu.ctypes.data, FAKE
+    a.h_out_slot, a.d_out_slot = out.ctypes.data, FAKE
+    if init is not None:
+        a.h_init_slot, a.d_init_slot = init.ctypes.data, FAKE
+    if ckpt is not None:
+        a.h_ckpt_slot, a.d_ckpt_slot = ckpt.ctypes.data, FAKE
+    return a
+
+
+def test_prefill_validation_errors():
+    p = HostPool()
+    s = [p.alloc()[1] for _ in range(6)]
+    cu, out = i32(0, 40, 64), i32(s[0], s[1])
+    # chunk not instantiated / interval not a multiple of the chunk
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, chunk=32)), None) == _abi.KDA_EUNSUPPORTED
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, interval=24)), None) == _abi.KDA_EUNSUPPORTED
+    # cu_seqlens must start at 0, not decrease, and end at n_tok
+    assert lib.kda_prefill(p.h, byref(prefill_args(i32(1, 40, 64), out)), None) == _abi.KDA_EINVAL
+    assert lib.kda_prefill(p.h, byref(prefill_args(i32(0, 40, 30), out)), None) == _abi.KDA_EINVAL
+    # checkpoints needed (40 // 16 + 24 // 16 = 3) but none given
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, interval=16)), None) == _abi.KDA_EINVAL
+    # out slots must be distinct; checkpoint slots distinct from out slots
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, i32(s[0], s[0]))), None) == _abi.KDA_EINVAL
+    ck = i32(s[2], s[3], s[1])
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, ckpt=ck, interval=16)), None) == _abi.KDA_EINVAL
+    # an init slot written by another sequence of the same call
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, init=i32(s[1], -1))), None) == _abi.KDA_EINVAL
+    # a non-live slot anywhere
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, i32(s[0], 7))), None) == _abi.KDA_EINVAL
+    # empty prefill is a no-op
+    assert lib.kda_prefill(p.h, byref(prefill_args(i32(0), i32())), None) == 0
+
+
+def test_mixed_batch_rejects_slot_overlap():
+    p = HostPool()
+    s = [p.alloc()[1] for _ in range(4)]
+    m = _abi.kda_mixed_args(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cu, out = i32(0, 32), i32(s[0])
+    m.prefill = prefill_args(cu, out)
+    dec, ver = i32(s[1], s[0]), i32(s[2])
+    m.n_decode, m.h_decode_slots, m.d_decode_slots = 2, dec.ctypes.data, FAKE
+    m.n_verify, m.n_pos, m.h_verify_slots, m.d_verify_slots = 1, 5, ver.ctypes.data, FAKE
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    assert lib.kda_slot_host_state(p.h, s[2]) == 1      # verify slot not marked pending
+
+
+def test_status_strings():
+    for st in range(-6, 1):
+        assert lib.kda_status_string(st)

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle on the same
+seeded inputs. Outputs within 2e-3 (``parity.rel_bf16``), states within 2e-3 (``parity.rel``),
+slot metadata and ring contents bit-exact, rejected drafts leave the state bit-identical.
+
+Workloads: the tiny d=16 case in full; the decode, verify/commit, 8192-token prefill and
+mixed 16384-token batch at their full sizes, with the oracle run on sampled heads where a
+full run would take minutes; mid-size ragged prefills in full."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kda_inputs as ki  # noqa: E402
+import recurrent_linear_attention_amd as kda  # noqa: E402
+from oracle import KDAPool as OPool  # noqa: E402
+from tests.parity import TOL, dev, f64, meta_equal, rel, rel_bf16  # noqa: E402
+
+
+def pools(n_slots, H, d, R=9, alloc=True):
+    g, o = kda.KDAPool(n_slots, H, d, R), OPool(n_slots, H, d, d, R)
+    if alloc:
+        for _ in range(n_slots):
+            assert g.kda_slot_alloc() == o.alloc()
+    return g, o
+
+
+def put_states(g, o, slots, states):
+    slots = [int(s) for s in slots]
+    g.state[slots] = states.to("cuda")
+    o.state[slots] = states.double().numpy()
+    torch.cuda.synchronize()
+
+
+def tok_dev(t: ki.Tokens):
+    return dev(t.q), dev(t.k), dev(t.v), dev(t.a), dev(t.b)
+
+
+def ring_check(g, o, slots):
+    rk, rv, ra, rb = g.ring_tensors()
+    for s in slots:
+        np.testing.assert_array_equal(f64(rk[s]), o.ring_k[s])
+        np.testing.assert_array_equal(f64(rv[s]), o.ring_v[s])
+        np.testing.assert_array_equal(f64(ra[s]), o.ring_a[s])
+        np.testing.assert_array_equal(f64(rb[s]), o.ring_b[s])
+
+
+def heads_np(t: ki.Tokens, heads):
+    return {n: x[..., heads, :] if x.ndim >= 3 and n != "b" else x[..., heads]
+            for n, x in t.np.items()}
+
+
+# ----------------------------------------------------------------------------- tiny, d = 16
+
+def test_tiny_prefill_checkpoints_verify_commit():
+    w = ki.tiny_workload(0)
+    H, d = w["H"], w["dk"]
+    g, o = pools(w["n_slots"], H, d, w["ring_cap"])
+    out, cks = 0, [1, 2, 3, 4]
+    pre = w["prefill"]
+    O = g.kda_prefill(*tok_dev(pre), w["cu_seqlens"], [out], ckpt_slots=cks,
+                      ckpt_interval=w["ckpt_interval"], chunk=w["chunk"])
+    Oo = o.prefill(pre.np, w["cu_seqlens"], [-1], [out], cks, w["ckpt_interval"])
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    for s in [out] + cks:
+        assert rel(g.state[s], o.state[s]) <= TOL, s
+    meta_equal(g.meta_array(), o.meta(), [out] + cks)
+    # the checkpoint after 64 tokens is the final state: the same bytes
+    assert torch.equal(g.state[cks[-1]], g.state[out])
+
+    ver = w["verify"]
+    before = g.state.clone()
+    Ov = g.kda_verify(*tok_dev(ver), [out])
+    Ovo = o.verify(ver.np, [out])
+    torch.cuda.synchronize()
+    assert rel_bf16(Ov, Ovo) <= TOL
+    assert torch.equal(g.state, before)
+    ring_check(g, o, [out])
+    meta_equal(g.meta_array(), o.meta(), [out])
+    assert g.host_state(out) == 2
+
+    na = torch.tensor(w["n_accepted"], dtype=torch.int32, device="cuda")
+    g.kda_commit([out], na)
+    o.commit([out], w["n_accepted"])
+    torch.cuda.synchronize()
+    assert rel(g.state[out], o.state[out]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), [out])
+    assert g.kda_read_device_error() == 0
+
+
+# ----------------------------------------------------------------------------- decode
+
+def test_decode_full_size():
+    w = ki.decode_workload(1)
+    g, o = pools(w["n_slots"], w["H"], w["dk"])
+    slots = w["slots"]
+    put_states(g, o, slots, w["states"])
+    untouched = [s for s in range(w["n_slots"]) if s not in set(slots.tolist())][:8]
+    before = g.state[untouched].clone()
+    O = g.kda_decode(*tok_dev(w["tokens"]), slots)
+    Oo = o.decode(w["tokens"].np, slots)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    assert torch.equal(g.state[untouched], before)
+    meta_equal(g.meta_array(), o.meta(), range(w["n_slots"]))
+
+
+# ----------------------------------------------------------------------------- verify / commit
+
+def test_verify_commit_rollback_full_size():
+    w = ki.verify_workload(2)
+    g, o = pools(w["n_slots"], w["H"], w["dk"], w["ring_cap"])
+    slots = w["slots"]
+    put_states(g, o, slots, w["states"])
+    tok = w["tokens"]
+    before = g.state.clone()
+    O = g.kda_verify(*tok_dev(tok), slots)
+    Oo = o.verify(tok.np, slots)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    assert torch.equal(g.state, before), "verify must not write any state"
+    ring_check(g, o, slots)
+    meta_equal(g.meta_array(), o.meta(), slots)
+
+    na = torch.from_numpy(w["n_accepted"]).to("cuda")
+    g.kda_commit(slots, na)
+    o.commit(slots, w["n_accepted"])
+    torch.cuda.synchronize()
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+
+    # replay == stepwise: 1 + n decode calls from the same state give the same bytes
+    g2, _ = pools(w["n_slots"], w["H"], w["dk"], w["ring_cap"])
+    g2.state.copy_(before)
+    for j in range(w["n_pos"]):
+        live = [i for i in range(len(slots)) if j <= w["n_accepted"][i]]
+        if not live:
+            break
+        sl = slots[live]
+        tj = [dev(x[live, j]) for x in (tok.q, tok.k, tok.v, tok.a, tok.b)]
+        g2.kda_decode(*tj, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(g2.state[slots.tolist()], g.state[slots.tolist()])
+
+    # a full reject: state bit-identical, pointer untouched
+    tok2 = ki.draw_tokens(np.random.default_rng(20), (len(slots), 5), w["H"], w["dk"], w["dk"])
+    snap = g.state.clone()
+    g.kda_verify(*tok_dev(tok2), slots)
+    o.verify(tok2.np, slots)
+    g.kda_rollback(slots)
+    o.rollback(slots)
+    torch.cuda.synchronize()
+    assert torch.equal(g.state, snap)
+    meta_equal(g.meta_array(), o.meta(), slots)
+    ring_check(g, o, slots)
+    assert g.kda_read_device_error() == 0
+
+
+def test_commit_out_of_range_acceptance_is_clamped_and_flagged():
+    w = ki.verify_workload(5, B=2, P=4)
+    g, o = pools(16, w["H"], w["dk"], 9)
+    slots = np.array([3, 9], dtype=np.int32)
+    put_states(g, o, slots, w["states"])
+    g.kda_verify(*tok_dev(w["tokens"]), slots)
+    o.verify(w["tokens"].np, slots)
+    na = [7, -2]
+    g.kda_commit(slots, torch.tensor(na, dtype=torch.int32, device="cuda"))
+    o.commit(slots, na)
+    assert g.kda_read_device_error() == kda._abi.KDA_DEVERR_NACC_RANGE
+    assert o.error_bits == kda._abi.KDA_DEVERR_NACC_RANGE
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+    assert g.kda_read_device_error() == 0     # reading clears the word
+
+
+def test_ring_wraps_over_many_rounds():
+    H, d, R = 4, 128, 9
+    g, o = pools(8, H, d, R)
+    rng = np.random.default_rng(30)
+    slots = np.array([1, 6], dtype=np.int32)
+    put_states(g, o, slots, ki.draw_states(rng, 2, H, d, d))
+    for r in range(6):
+        P = int(rng.integers(1, R + 1))
+        tok = ki.draw_tokens(rng, (2, P), H, d, d)
+        Og = g.kda_verify(*tok_dev(tok), slots)
+        Oo = o.verify(tok.np, slots)
+        if r % 3 == 2:
+            g.kda_rollback(slots)
+            o.rollback(slots)
+        else:
+            na = rng.integers(0, P, size=2).astype(np.int32)
+            g.kda_commit(slots, torch.from_numpy(na).to("cuda"))
+            o.commit(slots, na)
+        torch.cuda.synchronize()
+        assert rel_bf16(Og, Oo) <= TOL
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+    ring_check(g, o, slots)
+
+
+# ----------------------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_prefill_ragged_with_resume_and_checkpoints(d):
+    """Several sequences with ragged lengths (0, 1, chunk-1, chunk, chunk+1, several chunks),
+    some resuming from a slot, checkpoint export at every chunk*2 tokens."""
+    C = kda.chunk_for(d)
+    H = 4
+    lengths = [0, 1, C - 1, C, C + 1, 3 * C + 7, 5 * C]
+    n = len(lengths)
+    g, o = pools(40, H, d)
+    rng = np.random.default_rng(40 + d)
+    init = [-1, 20, -1, 21, -1, 22, 23]
+    put_states(g, o, [20, 21, 22, 23], ki.draw_states(rng, 4, H, d, d))
+    out = [0, 1, 2, 21, 4, 5, 6]            # sequence 3 updates its init slot in place
+    interval = 2 * C
+    n_ck = sum(L // interval for L in lengths)
+    cks = list(range(8, 8 + n_ck))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks,
+                      ckpt_interval=interval)
+    Oo = o.prefill(tok.np, cu, init, out, cks, interval)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    for s in out + cks:
+        assert rel(g.state[s], o.state[s]) <= TOL, s
+    meta_equal(g.meta_array(), o.meta(), out + cks)
+
+
+def test_prefill_full_size_sampled_heads():
+    w = ki.prefill_workload(3)
+    H, d = w["H"], w["dk"]
+    tok = w["tokens"]
+    n_ck = 8192 // w["ckpt_interval"]
+    g, _ = pools(64, H, d)
+    out, cks = 0, list(range(1, 1 + n_ck))
+    O = g.kda_prefill(*tok_dev(tok), w["cu_seqlens"], [out], ckpt_slots=cks,
+                      ckpt_interval=w["ckpt_interval"], chunk=w["chunk"])
+    torch.cuda.synchronize()
+    heads = [0, 17]
+    o = OPool(64, len(heads), d, d, 9)
+    for _ in range(64):
+        o.alloc()
+    Oo = o.prefill(heads_np(tok, heads), w["cu_seqlens"], [-1], [out], cks, w["ckpt_interval"])
+    assert rel_bf16(O[:, heads], Oo) <= TOL
+    for s in [out] + cks:
+        assert rel(g.state[s][heads], o.state[s]) <= TOL, s
+    meta_equal(g.meta_array(), o.meta(), [out] + cks)
+    assert torch.isfinite(O.float()).all()
+
+
+def test_prefill_is_deterministic():
+    w = ki.prefill_workload(7, lengths=(700, 300), H=8, ckpt_interval=128)
+    tok = w["tokens"]
+    res = []
+    for _ in range(2):
+        g, _ = pools(16, w["H"], w["dk"])
+        O = g.kda_prefill(*tok_dev(tok), w["cu_seqlens"], [0, 1], ckpt_slots=list(range(2, 9)),
+                          ckpt_interval=128)
+        torch.cuda.synchronize()
+        res.append((O.clone(), g.state.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+# ----------------------------------------------------------------------------- mixed batch
+
+def test_mixed_batch_full_size_sampled():
+    w = ki.mixed_workload(4)
+    H, d, P = w["H"], w["dk"], w["n_pos"]
+    g, o_all = pools(w["n_slots"], H, d, w["ring_cap"])
+    ds, vs, ps = w["decode_slots"], w["verify_slots"], w["prefill_slots"]
+    put_states(g, o_all, np.concatenate([ds, vs]), w["states"])
+    tok = w["tokens"]
+    O = g.kda_mixed_batch(*tok_dev(tok), w["cu_seqlens"], ps, ds, vs, P)
+    torch.cuda.synchronize()
+    n_pre = w["cu_seqlens"][-1]
+    nd = w["n_decode"]
+    # decode + verify parts: every head through the oracle
+    Od = o_all.decode(tok.slice(n_pre, n_pre + nd).np, ds)
+    vt = {n: x[n_pre + nd:].reshape((w["n_verify"], P) + x.shape[1:])
+          for n, x in tok.np.items()}
+    Ov = o_all.verify(vt, vs)
+    assert rel_bf16(O[n_pre:n_pre + nd], Od) <= TOL
+    assert rel_bf16(O[n_pre + nd:].reshape(w["n_verify"], P, H, d), Ov) <= TOL
+    assert rel(g.state[ds.tolist()], o_all.state[ds]) <= TOL
+    meta_equal(g.meta_array(), o_all.meta(), np.concatenate([ds, vs]))
+    ring_check(g, o_all, vs)
+    # prefill part: sampled heads
+    heads = [5, 30]
+    o = OPool(w["n_slots"], len(heads), d, d, 9)
+    for _ in range(w["n_slots"]):
+        o.alloc()
+    pre = tok.slice(0, n_pre)
+    Op = o.prefill(heads_np(pre, heads), w["cu_seqlens"], [-1] * len(ps), ps, [], 0)
+    assert rel_bf16(O[:n_pre, heads], Op) <= TOL
+    for s in ps:
+        assert rel(g.state[int(s)][heads], o.state[s]) <= TOL
+    # commit the verify part as the next step would
+    na = torch.from_numpy(w["n_accepted"]).to("cuda")
+    g.kda_commit(vs, na)
+    o_all.commit(vs, w["n_accepted"])
+    torch.cuda.synchronize()
+    assert rel(g.state[vs.tolist()], o_all.state[vs]) <= TOL
+    assert g.kda_read_device_error() == 0
+
+
+# ----------------------------------------------------------------------------- slot ops
+
+def test_slot_reset_and_checkpoint_copy():
+    H, d = 4, 128
+    g, o = pools(8, H, d)
+    rng = np.random.default_rng(50)
+    put_states(g, o, [2, 5], ki.draw_states(rng, 2, H, d, d))
+    tok = ki.draw_tokens(rng, (2,), H, d, d)
+    g.kda_decode(*tok_dev(tok), [2, 5])
+    o.decode(tok.np, [2, 5])
+    g.kda_slot_checkpoint(2, 7)
+    o.checkpoint(2, 7)
+    g.kda_slot_reset(5)
+    o.reset(5)
+    torch.cuda.synchronize()
+    assert torch.equal(g.state[7], g.state[2])
+    assert not g.state[5].any()
+    meta_equal(g.meta_array(), o.meta(), [2, 5, 7])
