@@ -47,6 +47,8 @@ typedef enum {
 /* Device error bits, accumulated in the pool's device error word. */
 #define KDA_DEVERR_NACC_RANGE 1u   /* commit got n_accepted outside [0, verified-1]; clamped */
 #define KDA_DEVERR_SLOT_RANGE 2u   /* a device slot array held an id outside the pool; skipped */
+#define KDA_DEVERR_DECAY_RANGE 4u  /* prefill: a key channel decayed by more than 2^-14 within 16
+                                      tokens; the fp16 operand of that block may lose accuracy */
 
 /* Pool geometry. ring_cap = positions a verify may hold (1 + max drafts), 1..64. */
 typedef struct {

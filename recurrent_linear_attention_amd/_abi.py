@@ -9,12 +9,18 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_int32, c_size_t, c_uint32, c_void_p
 
+# torch must load its HIP runtime before libkda.so does: both carry the soname
+# libamdhip64.so.7, so libkda.so then binds to torch's copy and the process holds a single
+# HIP/HSA runtime (two runtimes in one process do not share devices, streams or memory).
+import torch  # noqa: F401
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkda.so")
 
 KDA_OK, KDA_EINVAL, KDA_ENOSLOT, KDA_ESTATE, KDA_EUNSUPPORTED, KDA_EWORKSPACE, KDA_EHIP = \
     0, -1, -2, -3, -4, -5, -6
 KDA_DEVERR_NACC_RANGE = 1
 KDA_DEVERR_SLOT_RANGE = 2
+KDA_DEVERR_DECAY_RANGE = 4
 
 
 class kda_pool_desc(ctypes.Structure):
@@ -81,12 +87,24 @@ PROTOTYPES = {
 }
 
 
+def _check_single_runtime() -> None:
+    try:
+        maps = open("/proc/self/maps").read().splitlines()
+    except OSError:
+        return
+    hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    if len(hip) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(sorted(hip))
+                          + "); import torch before loading libkda.so")
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"KDA HIP library not found at {path}; build it with "
             "`python -m recurrent_linear_attention_amd.build` (there is no CPU fallback)")
     lib = ctypes.CDLL(path)
+    _check_single_runtime()
     for name, (res, args) in PROTOTYPES.items():
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args

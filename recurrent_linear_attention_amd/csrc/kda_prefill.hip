@@ -1,12 +1,569 @@
-// Chunked prefill dispatch (placeholder until the MFMA chunked kernel lands).
+// Chunked KDA prefill on gfx950 matrix cores, with the state checkpoint exported inside the
+// same pass ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "KDA checkpoints stay
+// inside the prefill").
+//
+// Chunked (WY/UT) form of the gated delta rule, for one head and one chunk of C tokens
+// (rows r, s) entered with state S (d x d, fp32). With G_r = sum_{t<=r} log2 a_t per key
+// channel:
+//     A_kk[r,s] = sum_i k_ri k_si 2^(G_ri - G_si)  (s < r),  A_qk likewise with q_r (s <= r)
+//     T  = (I + Diag(b) A_kk)^-1 Diag(b)
+//     X  = V - Kt S          Kt_r = k_r 2^(G_r)
+//     W  = T X               (the delta-rule innovations of the chunk)
+//     O  = Qt S + A_qk W     Qt_r = q_r 2^(G_r)
+//     S' = Diag(2^(G_C)) S + Kbar^T W,    Kbar_s = k_s 2^(G_C - G_s)
+// Derivation: write each step as S_r = Diag(a_r) S_{r-1} + k_r w_r^T and unroll over the chunk.
+//
+// Design for MI355X:
+//   * one work-group (8 waves, two per SIMD) per (sequence, head, slice of VS value columns).
+//     Value columns of S evolve independently, so slices need no exchange; the launcher picks
+//     VS in {16, 32, 64, 128} so that sequences x heads x slices roughly fills the CUs (a lone
+//     8192-token prompt at 32 heads runs 8 slices per head; a batch of 6 prompts runs whole
+//     heads). The S-independent part (A_kk, A_qk, T) is recomputed per slice.
+//   * all contractions run on v_mfma_f32_16x16x32_f16 / 16x16x16f16 with fp32 accumulation.
+//     fp16 operands (same rate as bf16, 3 more mantissa bits) keep the chunked form within
+//     2e-3 of the sequential fp64 result; bf16 operands do not (5e-3 in emulation). The state
+//     stays fp32 in MFMA accumulator registers across chunks; only operand copies are fp16.
+//   * every exponential factor is at most 1 except the column factor of the diagonal 16x16
+//     blocks of A_kk / A_qk, bounded by the 16-token decay of the block; beyond 2^14 on any
+//     channel the kernel flags KDA_DEVERR_DECAY_RANGE.
+//   * the next chunk's q/k/a/v/b are loaded into registers while the current chunk computes.
+//   * block ids are mapped so that all slices of one head run on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
 
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int PD = 128;           // head dim (dk = dv)
+constexpr int PC = 64;            // chunk
+constexpr int PNB = PC / 16;      // 16-row blocks per chunk
+constexpr int PNW = 8;            // waves per work-group
+constexpr int PNT = 64 * PNW;
+constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
+constexpr int PG = PD + 4;        // row pitch (floats) of the G array (16-row fragment reads hit
+                                  // every LDS bank exactly four times)
+constexpr int PC16 = PC + 8;      // row pitch (halves) of [.][PC] fp16 arrays
+constexpr int PL = PC + 8;        // row pitch (floats) of the fp32 [PC][PC] array
+constexpr int NPAIR = PNB * (PNB + 1) / 2;
+constexpr float DIAG_LOG2_LIMIT = 14.f;
+
+template <int VS>
+struct PfLds {
+  _Float16 kt[PC][P16];      // raw k (bf16 bits), then Kt in place
+  _Float16 qt[PC][P16];      // raw q (bf16 bits), then Qt in place
+  union {
+    float g[PC][PG];         // log2 a, then G
+    _Float16 s16t[VS][P16];  // S^T (fp16 operand copy)
+  } u1;
+  _Float16 kbt[PD][PC16];    // Kbar^T
+  union {
+    float l32[PC][PL];       // Diag(b) A_kk, strictly lower
+    _Float16 x16t[VS][PC16]; // X^T
+  } u2;
+  union {
+    float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
+    _Float16 w16t[VS][PC16]; // W^T
+  } u3;
+  _Float16 aqk[PC][PC16];    // A_qk, zero above the diagonal
+  _Float16 t16[PC][PC16];    // T, zero above the diagonal
+  float bsum[PNB][PD];       // per-block sums of log2 a
+  float ge[PNB][PD];         // G at the last row of each block
+  float gam[PD];             // 2^(G_C)
+  float b[PC];
+};
+
+__device__ __forceinline__ f4 mfma32(half8 a, half8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16(half4 a, half4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// Decay factors use the hardware exp2 / log2 (the fast path of HIP's math library): a result
+// below 2^-126 flushes to zero, which only drops contributions already below fp32 resolution.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __log2f(x); }
+
+__device__ __forceinline__ half8 ld8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+__device__ __forceinline__ void ld_f8(const float* p, float (&f)[8]) {
+  f4 x = *reinterpret_cast<const f4*>(p), y = *reinterpret_cast<const f4*>(p + 4);
+  f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3]; f[4] = y[0]; f[5] = y[1]; f[6] = y[2]; f[7] = y[3];
+}
+__device__ __forceinline__ void unpack8(const _Float16* raw, float (&f)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(raw);
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(ws[e] << 16);
+    f[2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ half4 to_h4(f4 x) {
+  return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+
+// Work-group barrier for LDS hand-offs inside the chunk loop: waits for this wave's LDS
+// operations only. Global loads (the next chunk's prefetch) and stores (outputs, checkpoints)
+// stay in flight across it; no wave of the work-group reads what another wave stores to global
+// memory in the loop, and the loop never reads a register before its load has been waited on.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// pair index p = P(P+1)/2 + Q for Q <= P
+__device__ __forceinline__ int pair_p(int p) { return p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0)); }
+
+// Column block Q of T = N Diag(b), N = (I + Diag(b) A_kk)^-1, from the diagonal inverses:
+// N_PQ = -N_PP sum_{Q<=R<P} L_PR N_RQ, 16x16x16 fp16 products with fp32 accumulation. The
+// accumulator layout of a 16x16x16 product equals its B-operand layout, so N_RQ stays in
+// registers from one product to the next.
+template <int Q, class Lds>
+__device__ __forceinline__ void t_column(Lds& L, int l16, int lq) {
+  f4 nq[PNB];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) nq[Q][e] = L.u3.nd[16 * Q + 4 * lq + e][l16];
+  const float bq = L.b[16 * Q + l16];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) L.t16[16 * Q + 4 * lq + e][16 * Q + l16] = (_Float16)(nq[Q][e] * bq);
+#pragma unroll
+  for (int Pb = Q + 1; Pb < PNB; ++Pb) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int R = Q; R < Pb; ++R) {
+      const f4 lr = *reinterpret_cast<const f4*>(&L.u2.l32[16 * Pb + l16][16 * R + 4 * lq]);
+      acc = mfma16(to_h4(lr), to_h4(nq[R]), acc);
+    }
+    const f4 np = *reinterpret_cast<const f4*>(&L.u3.nd[16 * Pb + l16][4 * lq]);
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    nq[Pb] = -mfma16(to_h4(np), to_h4(acc), zero);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) L.t16[16 * Pb + 4 * lq + e][16 * Q + l16] = (_Float16)(nq[Pb][e] * bq);
+  }
+}
+
+// Raw inputs of one chunk, held in registers between chunks (prefetch).
+template <int VS>
+struct Stage {
+  static constexpr int NCT = VS / 16;
+  static constexpr int NXT = (4 * NCT + PNW - 1) / PNW;   // X tiles per wave
+  uint4 k[PC * PD / 8 / PNT], q[PC * PD / 8 / PNT];
+  float4 a[PC * PD / 4 / PNT];
+  uint32_t v[NXT][4];     // V of the wave's X tiles: bf16 bits, rows 4*lq+e (kept unpacked so
+                          // that nothing waits on these loads before the next chunk)
+  float b;
+};
+
+template <int VS>
+__device__ __forceinline__ void load_stage(Stage<VS>& st, const PrefillLaunch& A, size_t tok0, int n,
+                                           int h, int H, int col0, int t, int w, int l16, int lq) {
+  constexpr int NK = PC * PD / 8 / PNT, NA = PC * PD / 4 / PNT, NCT = VS / 16;
+  const size_t hstride = (size_t)H * PD;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int idx = t + PNT * j, r = idx >> 4, c8 = (idx & 15) * 8;
+    uint4 kk = make_uint4(0, 0, 0, 0), qq = make_uint4(0, 0, 0, 0);
+    if (r < n) {
+      const size_t off = (tok0 + r) * hstride + (size_t)h * PD + c8;
+      kk = *reinterpret_cast<const uint4*>(A.t.k + off);
+      qq = *reinterpret_cast<const uint4*>(A.t.q + off);
+    }
+    st.k[j] = kk;
+    st.q[j] = qq;
+  }
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int idx = t + PNT * j, r = idx >> 5, c4 = (idx & 31) * 4;
+    float4 av = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (r < n) av = *reinterpret_cast<const float4*>(A.t.a + (tok0 + r) * hstride + (size_t)h * PD + c4);
+    st.a[j] = av;
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<VS>::NXT; ++j) {
+    const int it = w + PNW * j;
+    if (it < 4 * NCT) {
+      const int rt = it & 3, ct = it >> 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lq + e;
+        st.v[j][e] = r < n ? A.t.v[(tok0 + r) * hstride + (size_t)h * PD + col0 + 16 * ct + l16] : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.v[j][e] = 0u;
+    }
+  }
+  st.b = (t < n) ? A.t.b[(tok0 + t) * H + h] : 0.f;
+}
+
+template <int VS>
+__global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillLaunch A, int n_hg) {
+  constexpr int NVS = PD / VS, NCT = VS / 16;
+  constexpr int NS = 8 * NCT / PNW;                       // S tiles per wave
+  constexpr int NXT = Stage<VS>::NXT;
+  static_assert(8 * NCT % PNW == 0, "S tiles must divide among the waves");
+  __shared__ PfLds<VS> L;
+  const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
+  const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
+  if (hg >= n_hg) return;
+  const int H = P.H, si = hg / H, h = hg % H;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, l16 = l & 15, lq = l >> 4;
+
+  const int lo = A.cu_seqlens[si], hi = A.cu_seqlens[si + 1], len = hi - lo;
+  int ck = 0;
+  if (A.ckpt_interval > 0)
+    for (int j = 0; j < si; ++j) ck += (A.cu_seqlens[j + 1] - A.cu_seqlens[j]) / A.ckpt_interval;
+  const int init = A.init_slot ? A.init_slot[si] : -1;
+  const bool has_init = init >= 0 && init < P.num_slots;
+  const size_t per = (size_t)H * PD * PD, hoff = (size_t)h * PD * PD;
+  const int col0 = vs * VS;
+  const size_t hstride = (size_t)H * PD;
+
+  // State slice in accumulator layout. Wave w owns S tiles it = w + PNW*j: row tile
+  // it % 8 (key channels 16*rt + 4*lq + e), column tile it / 8 (col0 + 16*ct + l16).
+  f4 S[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + 4 * lq + e;
+      S[j][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] : 0.f;
+    }
+  }
+  const int64_t pos0 = has_init ? P.meta[init].pos : 0;
+
+  // T and A_qk are lower triangular; their upper blocks stay zero for the whole kernel.
+  for (int i = t; i < PC * PC16; i += PNT) {
+    (&L.aqk[0][0])[i] = (_Float16)0.f;
+    (&L.t16[0][0])[i] = (_Float16)0.f;
+  }
+
+  Stage<VS> st;
+  if (len > 0) load_stage<VS>(st, A, (size_t)lo, min(PC, len), h, H, col0, t, w, l16, lq);
+
+  for (int c0 = 0; c0 < len; c0 += PC) {
+    const int n = min(PC, len - c0);
+    const size_t tok0 = (size_t)(lo + c0);
+    lds_barrier();   // previous chunk's readers are done with every array below
+    // Lane indices re-derived through an opaque copy each chunk: LDS addresses are then
+    // recomputed per chunk instead of being hoisted out of the loop, where they would hold
+    // about a hundred VGPRs for the whole kernel.
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int t = tid, l = t & 63, l16 = l & 15, lq = l >> 4;
+
+    // ---- stage the chunk from registers (rows >= n: k = q = v = 0, a = 1, b = 0) -------
+    uint32_t vcur[NXT][4];
+#pragma unroll
+    for (int j = 0; j < PC * PD / 8 / PNT; ++j) {
+      const int idx = t + PNT * j, r = idx >> 4, c8 = (idx & 15) * 8;
+      *reinterpret_cast<uint4*>(&L.kt[r][c8]) = st.k[j];
+      *reinterpret_cast<uint4*>(&L.qt[r][c8]) = st.q[j];
+    }
+#pragma unroll
+    for (int j = 0; j < PC * PD / 4 / PNT; ++j) {
+      const int idx = t + PNT * j, r = idx >> 5, c4 = (idx & 31) * 4;
+      const f4 lg = {flog2(st.a[j].x), flog2(st.a[j].y), flog2(st.a[j].z), flog2(st.a[j].w)};
+      *reinterpret_cast<f4*>(&L.u1.g[r][c4]) = lg;
+    }
+    if (t < PC) L.b[t] = st.b;
+#pragma unroll
+    for (int j = 0; j < NXT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vcur[j][e] = st.v[j][e];
+    // prefetch the next chunk while this one computes
+    if (c0 + PC < len) load_stage<VS>(st, A, tok0 + PC, min(PC, len - c0 - PC), h, H, col0, t, w, l16, lq);
+    lds_barrier();
+
+    // ---- G = cumulative log2 a over rows; block-end values; gamma; decay-range check ----
+    if (t < 128) {
+      const int cq = (t & 31) * 4, Pb = t >> 5;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        f4* p = reinterpret_cast<f4*>(&L.u1.g[16 * Pb + r][cq]);
+        acc += *p;
+        *p = acc;
+      }
+      *reinterpret_cast<f4*>(&L.bsum[Pb][cq]) = acc;
+    }
+    lds_barrier();
+    if (t < 128) {
+      const int cq = (t & 31) * 4, Pb = t >> 5;
+      f4 pre = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < Pb; ++q) pre += *reinterpret_cast<const f4*>(&L.bsum[q][cq]);
+      const f4 bs = *reinterpret_cast<const f4*>(&L.bsum[Pb][cq]);
+      if (Pb > 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          f4* p = reinterpret_cast<f4*>(&L.u1.g[16 * Pb + r][cq]);
+          *p = *p + pre;
+        }
+      }
+      const f4 ge = pre + bs;
+      *reinterpret_cast<f4*>(&L.ge[Pb][cq]) = ge;
+      if (Pb == PNB - 1) {
+        *reinterpret_cast<f4*>(&L.gam[cq]) = f4{fexp2(ge[0]), fexp2(ge[1]), fexp2(ge[2]), fexp2(ge[3])};
+      }
+      if (-bs[0] > DIAG_LOG2_LIMIT || -bs[1] > DIAG_LOG2_LIMIT || -bs[2] > DIAG_LOG2_LIMIT ||
+          -bs[3] > DIAG_LOG2_LIMIT)
+        atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
+    }
+    lds_barrier();
+
+    // ---- A_kk, A_qk on matrix cores (one 16x16 block pair per item); Kbar^T alongside --
+    //      Operands: rows r of block P scaled by 2^(G_r - G_start(P)) (<= 1), columns s of
+    //      block Q by 2^(G_start(P) - G_s) (<= 1 for Q < P; the block's own decay for Q = P).
+    for (int p = w; p < NPAIR; p += PNW) {
+      const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
+      f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * Pb + l16, s = 16 * Q + l16;
+#pragma unroll 1
+      for (int kk = 0; kk < PD / 32; ++kk) {
+        const int c = 32 * kk + 8 * lq;
+        float kr[8], qr[8], ks[8], Gr[8], Gs[8], gs[8];
+        unpack8(&L.kt[r][c], kr);
+        unpack8(&L.qt[r][c], qr);
+        unpack8(&L.kt[s][c], ks);
+        ld_f8(&L.u1.g[r][c], Gr);
+        ld_f8(&L.u1.g[s][c], Gs);
+        if (Pb > 0) ld_f8(&L.ge[Pb - 1][c], gs);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gs[e] = 0.f;
+        }
+        half8 ak, aq, bb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float er = fexp2(Gr[e] - gs[e]);
+          ak[e] = (_Float16)(kr[e] * er);
+          aq[e] = (_Float16)(qr[e] * er);
+          bb[e] = (_Float16)(ks[e] * fexp2(gs[e] - Gs[e]));
+        }
+        akk = mfma32(ak, bb, akk);
+        aqk = mfma32(aq, bb, aqk);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * Pb + 4 * lq + e, ss = 16 * Q + l16;
+        L.u2.l32[rr][ss] = ss < rr ? L.b[rr] * akk[e] : 0.f;
+        L.aqk[rr][ss] = (_Float16)(ss <= rr ? aqk[e] : 0.f);
+      }
+    }
+    if (w >= NPAIR - PNW) {   // waves with a single pair also build Kbar^T
+      constexpr int NKB = PNW - (NPAIR - PNW);
+      for (int it = t - (NPAIR - PNW) * 64; it < PD * (PC / 8); it += NKB * 64) {
+        const int i = it % PD, s0 = (it / PD) * 8;
+        const float gc = L.ge[PNB - 1][i];
+        half8 kb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t raw = reinterpret_cast<const uint16_t*>(&L.kt[s0 + e][0])[i];
+          kb[e] = (_Float16)(__uint_as_float(raw << 16) * fexp2(gc - L.u1.g[s0 + e][i]));
+        }
+        *reinterpret_cast<half8*>(&L.kbt[i][s0]) = kb;
+      }
+    }
+    lds_barrier();
+
+    // ---- wave 0: diagonal blocks of (I + Diag(b) A_kk)^-1 by forward substitution;
+    //      others: Kt = k 2^G and Qt = q 2^G in place -------------------------------------
+    if (w == 0) {
+      const int Pb = lq, j = l16;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < r; ++s) acc = __builtin_fmaf(L.u2.l32[16 * Pb + r][16 * Pb + s], x[s], acc);
+        x[r] = (r == j ? 1.f : 0.f) - acc;
+        __builtin_amdgcn_sched_barrier(0);   // keep one row of L live at a time
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) L.u3.nd[16 * Pb + r][j] = x[r];
+    } else {
+      for (int it = t - 64; it < PC * (PD / 8); it += PNT - 64) {
+        const int r = it >> 4, c8 = (it & 15) * 8;
+        float kr[8], qr[8], G[8];
+        unpack8(&L.kt[r][c8], kr);
+        unpack8(&L.qt[r][c8], qr);
+        ld_f8(&L.u1.g[r][c8], G);
+        half8 kt, qt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float eg = fexp2(G[e]);
+          kt[e] = (_Float16)(kr[e] * eg);
+          qt[e] = (_Float16)(qr[e] * eg);
+        }
+        *reinterpret_cast<half8*>(&L.kt[r][c8]) = kt;
+        *reinterpret_cast<half8*>(&L.qt[r][c8]) = qt;
+      }
+    }
+    lds_barrier();
+
+    // ---- waves 0-3: T column blocks; then every wave: fp16 copy of its S^T tiles --------
+    if (w < PNB) {
+      switch (w) {
+        case 0: t_column<0>(L, l16, lq); break;
+        case 1: t_column<1>(L, l16, lq); break;
+        case 2: t_column<2>(L, l16, lq); break;
+        default: t_column<3>(L, l16, lq); break;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+      *reinterpret_cast<half4*>(&L.u1.s16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(S[j]);
+    }
+    lds_barrier();
+
+    // ---- X = V - Kt S --------------------------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < NXT; ++j) {
+      const int it = w + PNW * j;
+      if (it < 4 * NCT) {
+        const int rt = it & 3, ct = it >> 2;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < PD / 32; ++kk)
+          acc = mfma32(ld8(&L.kt[16 * rt + l16][32 * kk + 8 * lq]),
+                       ld8(&L.u1.s16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
+        f4 xv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[e] = __uint_as_float(vcur[j][e] << 16) - acc[e];
+        *reinterpret_cast<half4*>(&L.u2.x16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(xv);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+
+    // ---- W = T X (T is zero above the diagonal) --------------------------------------------
+#pragma unroll
+    for (int j = 0; j < NXT; ++j) {
+      const int it = w + PNW * j;
+      if (it < 4 * NCT) {
+        const int rt = it & 3, ct = it >> 2;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk <= (rt >> 1); ++kk)
+          acc = mfma32(ld8(&L.t16[16 * rt + l16][32 * kk + 8 * lq]),
+                       ld8(&L.u2.x16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
+        *reinterpret_cast<half4*>(&L.u3.w16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+
+    // ---- O = Qt S + A_qk W; S <- Diag(gamma) S + Kbar^T W -------------------------------------
+#pragma unroll
+    for (int j = 0; j < NXT; ++j) {
+      const int it = w + PNW * j;
+      if (it < 4 * NCT) {
+        const int rt = it & 3, ct = it >> 2;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < PD / 32; ++kk)
+          acc = mfma32(ld8(&L.qt[16 * rt + l16][32 * kk + 8 * lq]),
+                       ld8(&L.u1.s16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
+        for (int kk = 0; kk <= (rt >> 1); ++kk)
+          acc = mfma32(ld8(&L.aqk[16 * rt + l16][32 * kk + 8 * lq]),
+                       ld8(&L.u3.w16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * lq + e;
+          if (r < n) A.t.o[(tok0 + r) * hstride + (size_t)h * PD + col0 + 16 * ct + l16] = (uint16_t)f2bf(acc[e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[j][e] *= L.gam[16 * rt + 4 * lq + e];
+#pragma unroll
+      for (int kk = 0; kk < PC / 32; ++kk)
+        S[j] = mfma32(ld8(&L.kbt[16 * rt + l16][32 * kk + 8 * lq]),
+                      ld8(&L.u3.w16t[16 * ct + l16][32 * kk + 8 * lq]), S[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- checkpoint export inside the pass -------------------------------------------------
+    const int done = c0 + n;
+    if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
+      const int dst = A.ckpt_slot[ck++];
+      if (dst >= 0 && dst < P.num_slots) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rt + 4 * lq + e;
+            P.state[dst * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] = S[j][e];
+          }
+        }
+        if (t == 0 && h == 0 && vs == 0) {
+          kda_slot_meta mm{pos0 + done, 0, 0, 0, 0};
+          P.meta[dst] = mm;
+        }
+      }
+    }
+  }
+
+  const int out = A.out_slot[si];
+  if (out >= 0 && out < P.num_slots) {
+    __syncthreads();   // the init slot may be the out slot: every read of it is done
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * lq + e;
+        P.state[out * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] = S[j][e];
+      }
+    }
+    if (t == 0 && h == 0 && vs == 0) {
+      kda_slot_meta mm{pos0 + len, 0, 0, 0, 0};
+      P.meta[out] = mm;
+    }
+  }
+}
+
+int device_cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int VS>
+hipError_t launch_vs(const PoolView& p, const PrefillLaunch& a, int n_hg, hipStream_t s) {
+  const int blocks = ((n_hg + 7) / 8) * 8 * (PD / VS);
+  hipLaunchKernelGGL(prefill_chunk_kernel<VS>, dim3(blocks), dim3(PNT), 0, s, p, a, n_hg);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
-  return launch_prefill_recurrent(p, a, s);
+  if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
+  // One work-group per CU (LDS-bound): split value columns only while heads x sequences
+  // leave CUs idle.
+  const int n_hg = a.n_seq * p.H, cus = device_cu_count();
+  if (n_hg * 8 <= cus) return launch_vs<16>(p, a, n_hg, s);
+  if (n_hg * 4 <= cus) return launch_vs<32>(p, a, n_hg, s);
+  if (n_hg * 2 <= cus) return launch_vs<64>(p, a, n_hg, s);
+  return launch_vs<128>(p, a, n_hg, s);
 }
 
 }  // namespace kda

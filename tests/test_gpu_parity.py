@@ -233,6 +233,40 @@ def test_prefill_ragged_with_resume_and_checkpoints(d):
     meta_equal(g.meta_array(), o.meta(), out + cks)
 
 
+@pytest.mark.parametrize("H,n_seq", [(4, 7), (16, 3), (32, 3), (32, 5)])
+def test_prefill_every_slice_width(H, n_seq):
+    """sequences x heads of 28, 48, 96 and 160 select value-slice widths 16, 32, 64 and 128
+    on a 256-CU part; each must match the oracle (sampled heads, ragged lengths)."""
+    rng = np.random.default_rng(60 + H + n_seq)
+    lengths = [int(x) for x in rng.integers(1, 300, size=n_seq)]
+    lengths[0] = 257
+    d = 128
+    g, _ = pools(32, H, d)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    init = [-1] * n_seq
+    init[0] = 31
+    st = ki.draw_states(rng, 1, H, d, d)
+    g.state[31] = st[0].to("cuda")
+    out = list(range(n_seq))
+    interval = 128
+    n_ck = sum(L // interval for L in lengths)
+    cks = list(range(n_seq, n_seq + n_ck))
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks, ckpt_interval=interval)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    o = OPool(32, len(heads), d, d, 9)
+    for _ in range(32):
+        o.alloc()
+    o.state[31] = st[0][heads].double().numpy()
+    Oo = o.prefill(heads_np(tok, heads), cu, init, out, cks, interval)
+    assert rel_bf16(O[:, heads], Oo) <= TOL
+    for s in out + cks:
+        assert rel(g.state[s][heads], o.state[s]) <= TOL, s
+    meta_equal(g.meta_array(), o.meta(), out + cks)
+    assert g.kda_read_device_error() == 0
+
+
 def test_prefill_full_size_sampled_heads():
     w = ki.prefill_workload(3)
     H, d = w["H"], w["dk"]
