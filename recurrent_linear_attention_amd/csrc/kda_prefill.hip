@@ -16,9 +16,10 @@
 // Design for MI355X:
 //   * one work-group (8 waves, two per SIMD) per (sequence, head, slice of VS value columns).
 //     Value columns of S evolve independently, so slices need no exchange; the launcher picks
-//     VS in {16, 32, 64, 128} so that sequences x heads x slices roughly fills the CUs (a lone
-//     8192-token prompt at 32 heads runs 8 slices per head; a batch of 6 prompts runs whole
-//     heads). The S-independent part (A_kk, A_qk, T) is recomputed per slice.
+//     VS in {16, 32, 64, 128} so that sequences x heads x slices stays within two rounds of
+//     CUs (a lone 8192-token prompt at 32 heads runs 8 slices per head, a batch of 6 prompts
+//     2 slices), and work-groups start longest sequence first. The S-independent part
+//     (A_kk, A_qk, T) is recomputed per slice.
 //   * all contractions run on v_mfma_f32_16x16x32_f16 / 16x16x16f16 with fp32 accumulation.
 //     fp16 operands (same rate as bf16, 3 more mantissa bits) keep the chunked form within
 //     2e-3 of the sequential fp64 result; bf16 operands do not (5e-3 in emulation). The state
@@ -55,10 +56,13 @@ constexpr float DIAG_LOG2_LIMIT = 14.f;
 
 template <int VS>
 struct PfLds {
-  _Float16 kt[PC][P16];      // raw k (bf16 bits), then Kt in place
-  _Float16 qt[PC][P16];      // raw q (bf16 bits), then Qt in place
+  _Float16 kt[PC][P16];      // Kt = k 2^G (fp16)
+  _Float16 qt[PC][P16];      // Qt = q 2^G (fp16)
   union {
-    float g[PC][PG];         // log2 a, then G
+    struct {                 // A-operands of A_kk / A_qk: rows of block P times 2^(G - G_start(P))
+      _Float16 ka[PC][P16];
+      _Float16 qa[PC][P16];
+    } a;
     _Float16 s16t[VS][P16];  // S^T (fp16 operand copy)
   } u1;
   _Float16 kbt[PD][PC16];    // Kbar^T
@@ -67,12 +71,15 @@ struct PfLds {
     _Float16 x16t[VS][PC16]; // X^T
   } u2;
   union {
-    float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
+    _Float16 f16[PC][P16];   // F_s = k_s 2^(G_end(block of s) - G_s)
     _Float16 w16t[VS][PC16]; // W^T
   } u3;
   _Float16 aqk[PC][PC16];    // A_qk, zero above the diagonal
   _Float16 t16[PC][PC16];    // T, zero above the diagonal
-  float bsum[PNB][PD];       // per-block sums of log2 a
+  union {
+    float part[PC / 4][PD];  // sums of log2 a over each group of 4 rows
+    float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
+  } u4;
   float ge[PNB][PD];         // G at the last row of each block
   float gam[PD];             // 2^(G_C)
   float b[PC];
@@ -115,6 +122,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Index of the sequence with the given rank in descending length order (ties: lower index
+// first). Uniform across the work-group; O(n_seq^2), used once per work-group.
+__device__ __forceinline__ int seq_by_rank(const int32_t* cu, int n_seq, int rank) {
+  if (n_seq > 256) return rank;
+  for (int j = 0; j < n_seq; ++j) {
+    const int lj = cu[j + 1] - cu[j];
+    int rj = 0;
+    for (int k = 0; k < n_seq; ++k) {
+      const int lk = cu[k + 1] - cu[k];
+      rj += (lk > lj) || (lk == lj && k < j);
+    }
+    if (rj == rank) return j;
+  }
+  return rank;
+}
+
 // pair index p = P(P+1)/2 + Q for Q <= P
 __device__ __forceinline__ int pair_p(int p) { return p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0)); }
 
@@ -126,7 +149,7 @@ template <int Q, class Lds>
 __device__ __forceinline__ void t_column(Lds& L, int l16, int lq) {
   f4 nq[PNB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) nq[Q][e] = L.u3.nd[16 * Q + 4 * lq + e][l16];
+  for (int e = 0; e < 4; ++e) nq[Q][e] = L.u4.nd[16 * Q + 4 * lq + e][l16];
   const float bq = L.b[16 * Q + l16];
 #pragma unroll
   for (int e = 0; e < 4; ++e) L.t16[16 * Q + 4 * lq + e][16 * Q + l16] = (_Float16)(nq[Q][e] * bq);
@@ -138,7 +161,7 @@ __device__ __forceinline__ void t_column(Lds& L, int l16, int lq) {
       const f4 lr = *reinterpret_cast<const f4*>(&L.u2.l32[16 * Pb + l16][16 * R + 4 * lq]);
       acc = mfma16(to_h4(lr), to_h4(nq[R]), acc);
     }
-    const f4 np = *reinterpret_cast<const f4*>(&L.u3.nd[16 * Pb + l16][4 * lq]);
+    const f4 np = *reinterpret_cast<const f4*>(&L.u4.nd[16 * Pb + l16][4 * lq]);
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
     nq[Pb] = -mfma16(to_h4(np), to_h4(acc), zero);
 #pragma unroll
@@ -146,13 +169,15 @@ __device__ __forceinline__ void t_column(Lds& L, int l16, int lq) {
   }
 }
 
-// Raw inputs of one chunk, held in registers between chunks (prefetch).
+// Raw inputs of one chunk, held in registers between chunks (prefetch). Thread t owns key
+// rows 4m .. 4m+3 (m = t / 32) and key channels 4cq .. 4cq+3 (cq = t % 32): a row of 32
+// threads reads 256 contiguous bytes of q / k and 512 of a.
 template <int VS>
 struct Stage {
   static constexpr int NCT = VS / 16;
   static constexpr int NXT = (4 * NCT + PNW - 1) / PNW;   // X tiles per wave
-  uint4 k[PC * PD / 8 / PNT], q[PC * PD / 8 / PNT];
-  float4 a[PC * PD / 4 / PNT];
+  uint2 k[4], q[4];       // 4 bf16 each
+  float4 a[4];
   uint32_t v[NXT][4];     // V of the wave's X tiles: bf16 bits, rows 4*lq+e (kept unpacked so
                           // that nothing waits on these loads before the next chunk)
   float b;
@@ -161,26 +186,23 @@ struct Stage {
 template <int VS>
 __device__ __forceinline__ void load_stage(Stage<VS>& st, const PrefillLaunch& A, size_t tok0, int n,
                                            int h, int H, int col0, int t, int w, int l16, int lq) {
-  constexpr int NK = PC * PD / 8 / PNT, NA = PC * PD / 4 / PNT, NCT = VS / 16;
+  constexpr int NCT = VS / 16;
   const size_t hstride = (size_t)H * PD;
+  const int m = t >> 5, c4 = (t & 31) * 4;
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int idx = t + PNT * j, r = idx >> 4, c8 = (idx & 15) * 8;
-    uint4 kk = make_uint4(0, 0, 0, 0), qq = make_uint4(0, 0, 0, 0);
-    if (r < n) {
-      const size_t off = (tok0 + r) * hstride + (size_t)h * PD + c8;
-      kk = *reinterpret_cast<const uint4*>(A.t.k + off);
-      qq = *reinterpret_cast<const uint4*>(A.t.q + off);
-    }
-    st.k[j] = kk;
-    st.q[j] = qq;
-  }
-#pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int idx = t + PNT * j, r = idx >> 5, c4 = (idx & 31) * 4;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * m + i;
+    uint2 kk = make_uint2(0, 0), qq = make_uint2(0, 0);
     float4 av = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (r < n) av = *reinterpret_cast<const float4*>(A.t.a + (tok0 + r) * hstride + (size_t)h * PD + c4);
-    st.a[j] = av;
+    if (r < n) {
+      const size_t off = (tok0 + r) * hstride + (size_t)h * PD + c4;
+      kk = *reinterpret_cast<const uint2*>(A.t.k + off);
+      qq = *reinterpret_cast<const uint2*>(A.t.q + off);
+      av = *reinterpret_cast<const float4*>(A.t.a + off);
+    }
+    st.k[i] = kk;
+    st.q[i] = qq;
+    st.a[i] = av;
   }
 #pragma unroll
   for (int j = 0; j < Stage<VS>::NXT; ++j) {
@@ -210,7 +232,10 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
   const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
   const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
   if (hg >= n_hg) return;
-  const int H = P.H, si = hg / H, h = hg % H;
+  // Work-groups are dispatched in block order: sequence rank 0 (the longest; ties by index)
+  // first, so the longest recurrences start before the short ones fill the remaining CUs.
+  const int H = P.H, h = hg % H;
+  const int si = seq_by_rank(A.cu_seqlens, A.n_seq, hg / H);
   const int t = threadIdx.x, w = t >> 6, l = t & 63, l16 = l & 15, lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], hi = A.cu_seqlens[si + 1], len = hi - lo;
@@ -257,21 +282,24 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
     asm volatile("" : "+v"(tid));
     const int t = tid, l = t & 63, l16 = l & 15, lq = l >> 4;
 
-    // ---- stage the chunk from registers (rows >= n: k = q = v = 0, a = 1, b = 0) -------
-    uint32_t vcur[NXT][4];
+    // ---- G = cumulative log2 a over the chunk's rows, per key channel: in registers over
+    //      the thread's 4 rows, then one exchange of the 16 row-group sums through LDS ------
+    const int m4 = t >> 5, c4 = (t & 31) * 4, Pm = m4 >> 2;
+    uint2 kcur[4], qcur[4];
+    f4 Gl[4];
+    {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < PC * PD / 8 / PNT; ++j) {
-      const int idx = t + PNT * j, r = idx >> 4, c8 = (idx & 15) * 8;
-      *reinterpret_cast<uint4*>(&L.kt[r][c8]) = st.k[j];
-      *reinterpret_cast<uint4*>(&L.qt[r][c8]) = st.q[j];
-    }
-#pragma unroll
-    for (int j = 0; j < PC * PD / 4 / PNT; ++j) {
-      const int idx = t + PNT * j, r = idx >> 5, c4 = (idx & 31) * 4;
-      const f4 lg = {flog2(st.a[j].x), flog2(st.a[j].y), flog2(st.a[j].z), flog2(st.a[j].w)};
-      *reinterpret_cast<f4*>(&L.u1.g[r][c4]) = lg;
+      for (int i = 0; i < 4; ++i) {
+        acc += f4{flog2(st.a[i].x), flog2(st.a[i].y), flog2(st.a[i].z), flog2(st.a[i].w)};
+        Gl[i] = acc;
+        kcur[i] = st.k[i];
+        qcur[i] = st.q[i];
+      }
+      *reinterpret_cast<f4*>(&L.u4.part[m4][c4]) = acc;
     }
     if (t < PC) L.b[t] = st.b;
+    uint32_t vcur[NXT][4];
 #pragma unroll
     for (int j = 0; j < NXT; ++j)
 #pragma unroll
@@ -280,128 +308,143 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
     if (c0 + PC < len) load_stage<VS>(st, A, tok0 + PC, min(PC, len - c0 - PC), h, H, col0, t, w, l16, lq);
     lds_barrier();
 
-    // ---- G = cumulative log2 a over rows; block-end values; gamma; decay-range check ----
-    if (t < 128) {
-      const int cq = (t & 31) * 4, Pb = t >> 5;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- decayed fp16 operands from registers: Ka/Qa (rows of block P times 2^(G - G_start(P))),
+    //      F (times 2^(G_end(P) - G)), Kt/Qt (times 2^G); every factor is <= 1. Each thread sums
+    //      the row-group totals in the same order, so G at a block's last row equals G_end. ------
+    {
+      // Row-group sums in increasing order (unrolled, with a wave-uniform bound, so the loads
+      // issue back to back): gs = G before the block, pre = G before the thread's rows,
+      // gend = G at the block's last row.
+      f4 gs = {0.f, 0.f, 0.f, 0.f}, pre, gend;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        f4* p = reinterpret_cast<f4*>(&L.u1.g[16 * Pb + r][cq]);
-        acc += *p;
-        *p = acc;
-      }
-      *reinterpret_cast<f4*>(&L.bsum[Pb][cq]) = acc;
-    }
-    lds_barrier();
-    if (t < 128) {
-      const int cq = (t & 31) * 4, Pb = t >> 5;
-      f4 pre = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < Pb; ++q) pre += *reinterpret_cast<const f4*>(&L.bsum[q][cq]);
-      const f4 bs = *reinterpret_cast<const f4*>(&L.bsum[Pb][cq]);
-      if (Pb > 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          f4* p = reinterpret_cast<f4*>(&L.u1.g[16 * Pb + r][cq]);
-          *p = *p + pre;
+      for (int mm = 0; mm < PC / 4; ++mm) {
+        if (mm == 4 * Pm) pre = gs;
+        if (mm == m4) gend = pre;
+        if (mm < 4 * Pm + 4) {
+          const f4 pv = *reinterpret_cast<const f4*>(&L.u4.part[mm][c4]);
+          if (mm < 4 * Pm) gs += pv;
+          else if (mm < m4) pre += pv;
+          else gend += pv;
         }
       }
-      const f4 ge = pre + bs;
-      *reinterpret_cast<f4*>(&L.ge[Pb][cq]) = ge;
-      if (Pb == PNB - 1) {
-        *reinterpret_cast<f4*>(&L.gam[cq]) = f4{fexp2(ge[0]), fexp2(ge[1]), fexp2(ge[2]), fexp2(ge[3])};
+      if ((m4 & 3) == 3) {
+        *reinterpret_cast<f4*>(&L.ge[Pm][c4]) = gend;
+        if (Pm == PNB - 1)
+          *reinterpret_cast<f4*>(&L.gam[c4]) = f4{fexp2(gend[0]), fexp2(gend[1]), fexp2(gend[2]), fexp2(gend[3])};
+        const f4 dec = gs - gend;   // log2 of the inverse decay of this block, >= 0
+        if (dec[0] > DIAG_LOG2_LIMIT || dec[1] > DIAG_LOG2_LIMIT || dec[2] > DIAG_LOG2_LIMIT ||
+            dec[3] > DIAG_LOG2_LIMIT)
+          atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
       }
-      if (-bs[0] > DIAG_LOG2_LIMIT || -bs[1] > DIAG_LOG2_LIMIT || -bs[2] > DIAG_LOG2_LIMIT ||
-          -bs[3] > DIAG_LOG2_LIMIT)
-        atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
-    }
-    lds_barrier();
-
-    // ---- A_kk, A_qk on matrix cores (one 16x16 block pair per item); Kbar^T alongside --
-    //      Operands: rows r of block P scaled by 2^(G_r - G_start(P)) (<= 1), columns s of
-    //      block Q by 2^(G_start(P) - G_s) (<= 1 for Q < P; the block's own decay for Q = P).
-    for (int p = w; p < NPAIR; p += PNW) {
-      const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
-      f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * Pb + l16, s = 16 * Q + l16;
-#pragma unroll 1
-      for (int kk = 0; kk < PD / 32; ++kk) {
-        const int c = 32 * kk + 8 * lq;
-        float kr[8], qr[8], ks[8], Gr[8], Gs[8], gs[8];
-        unpack8(&L.kt[r][c], kr);
-        unpack8(&L.qt[r][c], qr);
-        unpack8(&L.kt[s][c], ks);
-        ld_f8(&L.u1.g[r][c], Gr);
-        ld_f8(&L.u1.g[s][c], Gs);
-        if (Pb > 0) ld_f8(&L.ge[Pb - 1][c], gs);
-        else {
+      const f4 y = {fexp2(gs[0]), fexp2(gs[1]), fexp2(gs[2]), fexp2(gs[3])};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) gs[e] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * m4 + i;
+        const float kr[4] = {__uint_as_float(kcur[i].x << 16), __uint_as_float(kcur[i].x & 0xffff0000u),
+                             __uint_as_float(kcur[i].y << 16), __uint_as_float(kcur[i].y & 0xffff0000u)};
+        const float qr[4] = {__uint_as_float(qcur[i].x << 16), __uint_as_float(qcur[i].x & 0xffff0000u),
+                             __uint_as_float(qcur[i].y << 16), __uint_as_float(qcur[i].y & 0xffff0000u)};
+        half4 hka, hqa, hkt, hqt, hf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float G = pre[e] + Gl[i][e];
+          const float e1 = fexp2(G - gs[e]);
+          const float ka = kr[e] * e1, qa = qr[e] * e1;
+          hka[e] = (_Float16)ka;
+          hqa[e] = (_Float16)qa;
+          hkt[e] = (_Float16)(ka * y[e]);
+          hqt[e] = (_Float16)(qa * y[e]);
+          hf[e] = (_Float16)(kr[e] * fexp2(gend[e] - G));
         }
-        half8 ak, aq, bb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float er = fexp2(Gr[e] - gs[e]);
-          ak[e] = (_Float16)(kr[e] * er);
-          aq[e] = (_Float16)(qr[e] * er);
-          bb[e] = (_Float16)(ks[e] * fexp2(gs[e] - Gs[e]));
-        }
-        akk = mfma32(ak, bb, akk);
-        aqk = mfma32(aq, bb, aqk);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * Pb + 4 * lq + e, ss = 16 * Q + l16;
-        L.u2.l32[rr][ss] = ss < rr ? L.b[rr] * akk[e] : 0.f;
-        L.aqk[rr][ss] = (_Float16)(ss <= rr ? aqk[e] : 0.f);
-      }
-    }
-    if (w >= NPAIR - PNW) {   // waves with a single pair also build Kbar^T
-      constexpr int NKB = PNW - (NPAIR - PNW);
-      for (int it = t - (NPAIR - PNW) * 64; it < PD * (PC / 8); it += NKB * 64) {
-        const int i = it % PD, s0 = (it / PD) * 8;
-        const float gc = L.ge[PNB - 1][i];
-        half8 kb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t raw = reinterpret_cast<const uint16_t*>(&L.kt[s0 + e][0])[i];
-          kb[e] = (_Float16)(__uint_as_float(raw << 16) * fexp2(gc - L.u1.g[s0 + e][i]));
-        }
-        *reinterpret_cast<half8*>(&L.kbt[i][s0]) = kb;
+        *reinterpret_cast<half4*>(&L.u1.a.ka[r][c4]) = hka;
+        *reinterpret_cast<half4*>(&L.u1.a.qa[r][c4]) = hqa;
+        *reinterpret_cast<half4*>(&L.kt[r][c4]) = hkt;
+        *reinterpret_cast<half4*>(&L.qt[r][c4]) = hqt;
+        *reinterpret_cast<half4*>(&L.u3.f16[r][c4]) = hf;
       }
     }
     lds_barrier();
 
-    // ---- wave 0: diagonal blocks of (I + Diag(b) A_kk)^-1 by forward substitution;
-    //      others: Kt = k 2^G and Qt = q 2^G in place -------------------------------------
-    if (w == 0) {
-      const int Pb = lq, j = l16;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) acc = __builtin_fmaf(L.u2.l32[16 * Pb + r][16 * Pb + s], x[s], acc);
-        x[r] = (r == j ? 1.f : 0.f) - acc;
-        __builtin_amdgcn_sched_barrier(0);   // keep one row of L live at a time
+    // ---- A_kk, A_qk block pairs on matrix cores. Waves 0-3: diagonal pair (w, w), then the
+    //      inverse of that block by forward substitution (the wave's own LDS writes, no
+    //      barrier needed). Waves 4-7: the six off-diagonal pairs; waves 6-7 also Kbar^T. -----
+    {
+      // pair index p = P(P+1)/2 + Q: diagonal pairs 0, 2, 5, 9; off-diagonal 1, 3, 4, 6, 7, 8
+      int pa, pb;
+      switch (w) {
+        case 0: pa = 0; pb = -1; break;
+        case 1: pa = 2; pb = -1; break;
+        case 2: pa = 5; pb = -1; break;
+        case 3: pa = 9; pb = -1; break;
+        case 4: pa = 1; pb = 7; break;
+        case 5: pa = 3; pb = 8; break;
+        case 6: pa = 4; pb = -1; break;
+        default: pa = 6; pb = -1; break;
       }
+      for (int pi = 0; pi < 2; ++pi) {
+        const int p = pi == 0 ? pa : pb;
+        if (p < 0) break;
+        const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
+        f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) L.u3.nd[16 * Pb + r][j] = x[r];
-    } else {
-      for (int it = t - 64; it < PC * (PD / 8); it += PNT - 64) {
-        const int r = it >> 4, c8 = (it & 15) * 8;
-        float kr[8], qr[8], G[8];
-        unpack8(&L.kt[r][c8], kr);
-        unpack8(&L.qt[r][c8], qr);
-        ld_f8(&L.u1.g[r][c8], G);
-        half8 kt, qt;
+        for (int kk = 0; kk < PD / 32; ++kk) {
+          const int c = 32 * kk + 8 * lq;
+          const half8 fk = ld8(&L.u3.f16[16 * Q + l16][c]);
+          float gsP[8], geQ[8];
+          if (Pb > 0) ld_f8(&L.ge[Pb - 1][c], gsP);
+          else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float eg = fexp2(G[e]);
-          kt[e] = (_Float16)(kr[e] * eg);
-          qt[e] = (_Float16)(qr[e] * eg);
+            for (int e = 0; e < 8; ++e) gsP[e] = 0.f;
+          }
+          ld_f8(&L.ge[Q][c], geQ);
+          half8 bb;   // k_s 2^(G_start(P) - G_s) = F_s 2^(G_start(P) - G_end(Q))
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bb[e] = (_Float16)((float)fk[e] * fexp2(gsP[e] - geQ[e]));
+          akk = mfma32(ld8(&L.u1.a.ka[16 * Pb + l16][c]), bb, akk);
+          aqk = mfma32(ld8(&L.u1.a.qa[16 * Pb + l16][c]), bb, aqk);
         }
-        *reinterpret_cast<half8*>(&L.kt[r][c8]) = kt;
-        *reinterpret_cast<half8*>(&L.qt[r][c8]) = qt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * Pb + 4 * lq + e, ss = 16 * Q + l16;
+          L.u2.l32[rr][ss] = ss < rr ? L.b[rr] * akk[e] : 0.f;
+          L.aqk[rr][ss] = (_Float16)(ss <= rr ? aqk[e] : 0.f);
+        }
+      }
+      if (w < PNB) {
+        if (l < 16) {   // column j of the inverse of the diagonal block w
+          const int Pb = w, j = l;
+          // lane j holds row j of the block; row r's entries are broadcast with readlane
+          float rowv[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f4 rr = *reinterpret_cast<const f4*>(&L.u2.l32[16 * Pb + j][16 * Pb + 4 * q4]);
+            rowv[4 * q4] = rr[0]; rowv[4 * q4 + 1] = rr[1]; rowv[4 * q4 + 2] = rr[2]; rowv[4 * q4 + 3] = rr[3];
+          }
+          float x[16];
+          x[0] = j == 0 ? 1.f : 0.f;
+#pragma unroll
+          for (int r = 1; r < 16; ++r) {
+            // x_r = [r == j] - sum_{s<r} L_rs x_s, as four interleaved partial sums
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < r; ++s) {
+              const float lrs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rowv[s]), r));
+              acc[s & 3] = __builtin_fmaf(lrs, x[s], acc[s & 3]);
+            }
+            x[r] = (r == j ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) L.u4.nd[16 * Pb + r][j] = x[r];
+        }
+      } else if (w >= PNB + 2) {   // Kbar^T = (F * zv)^T
+        for (int it = t - (PNB + 2) * 64; it < PD * (PC / 8); it += (PNW - PNB - 2) * 64) {
+          const int i = it % PD, s0 = (it / PD) * 8, Q = s0 >> 4;
+          const float z = fexp2(L.ge[PNB - 1][i] - L.ge[Q][i]);
+          half8 kb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kb[e] = (_Float16)((float)L.u3.f16[s0 + e][i] * z);
+          *reinterpret_cast<half8*>(&L.kbt[i][s0]) = kb;
+        }
       }
     }
     lds_barrier();
@@ -557,12 +600,13 @@ hipError_t launch_vs(const PoolView& p, const PrefillLaunch& a, int n_hg, hipStr
 
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
   if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
-  // One work-group per CU (LDS-bound): split value columns only while heads x sequences
-  // leave CUs idle.
+  // One work-group per CU (LDS-bound). The per-chunk latency of a chain depends little on
+  // the slice width (the S-independent part dominates), so split value columns as long as
+  // the grid stays within two rounds of CUs; work-groups start longest sequence first.
   const int n_hg = a.n_seq * p.H, cus = device_cu_count();
-  if (n_hg * 8 <= cus) return launch_vs<16>(p, a, n_hg, s);
-  if (n_hg * 4 <= cus) return launch_vs<32>(p, a, n_hg, s);
-  if (n_hg * 2 <= cus) return launch_vs<64>(p, a, n_hg, s);
+  if (n_hg * 8 <= 2 * cus) return launch_vs<16>(p, a, n_hg, s);
+  if (n_hg * 4 <= 2 * cus) return launch_vs<32>(p, a, n_hg, s);
+  if (n_hg * 2 <= 2 * cus) return launch_vs<64>(p, a, n_hg, s);
   return launch_vs<128>(p, a, n_hg, s);
 }
 

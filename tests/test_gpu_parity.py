@@ -233,9 +233,9 @@ def test_prefill_ragged_with_resume_and_checkpoints(d):
     meta_equal(g.meta_array(), o.meta(), out + cks)
 
 
-@pytest.mark.parametrize("H,n_seq", [(4, 7), (16, 3), (32, 3), (32, 5)])
+@pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 3), (32, 6), (32, 9)])
 def test_prefill_every_slice_width(H, n_seq):
-    """sequences x heads of 28, 48, 96 and 160 select value-slice widths 16, 32, 64 and 128
+    """sequences x heads of 28, 96, 192 and 288 select value-slice widths 16, 32, 64 and 128
     on a 256-CU part; each must match the oracle (sampled heads, ragged lengths)."""
     rng = np.random.default_rng(60 + H + n_seq)
     lengths = [int(x) for x in rng.integers(1, 300, size=n_seq)]
