@@ -36,6 +36,25 @@ TOK_OUT_B = D * 2                           # o bf16
 RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
 
 
+# HBM traffic of one prefill launch of the mixed step, from rocprofv3 counter passes
+# (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) scaled by the counters' reading for a 1 GiB
+# device copy (FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them: factors 2.0 and
+# 1.0). Valid only for the kernel source it was measured on (first 16 hex digits of its
+# SHA-256); for any other source the bench reports traffic as null.
+PREFILL_TRAFFIC = {"source_sha256_16": "9f2fb1fffd275d77", "fetch_kib": 334688, "fetch_scale": 2.0,
+                   "write_kib": 142816, "write_scale": 1.0}
+
+
+def prefill_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "recurrent_linear_attention_amd", "csrc", "kda_prefill.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    t = PREFILL_TRAFFIC
+    if sha != t["source_sha256_16"]:
+        return None
+    return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
+
+
 def prefill_bytes(n_tok, H, n_out, n_init=0, n_ckpt=0):
     return n_tok * H * (TOK_IN_B + TOK_OUT_B) + (n_out + n_init + n_ckpt) * H * STATE_B
 
@@ -103,7 +122,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (a known-size reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "repeats": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the KDA hot path shards by heads and sequences "
               "with no exchange, and this build runs on a single MI355X (--gpus 1).",
@@ -186,7 +218,7 @@ def main():
     kernels["prefill"]["mfma_frac"] = round(pf / ms["prefill"] / 1e9 / MFMA_PEAK_TFLOPS, 4)
     pre_gbs = byts["prefill"] / ms["prefill"] / 1e6
     roofline = {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": prefill_traffic_bytes(),
                 "kernel": "prefill (chunked, all sequences of the batch in one launch)",
                 "alg_bytes_per_launch": byts["prefill"]}
 
