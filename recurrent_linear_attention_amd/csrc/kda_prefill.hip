@@ -81,6 +81,7 @@ struct PfLds {
     float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
   } u4;
   float ge[PNB][PD];         // G at the last row of each block
+  _Float16 xvh[NPAIR][PD];   // 2^(G_start(P) - G_end(Q)) per pair, fp16
   float gam[PD];             // 2^(G_C)
   float b[PC];
 };
@@ -110,9 +111,8 @@ __device__ __forceinline__ void unpack8(const _Float16* raw, float (&f)[8]) {
     f[2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
   }
 }
-__device__ __forceinline__ half4 to_h4(f4 x) {
-  return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-}
+// fp32 -> fp16 (round to nearest even) as packed conversions (v_cvt_pk_f16_f32)
+__device__ __forceinline__ half4 to_h4(f4 x) { return __builtin_convertvector(x, half4); }
 
 // Work-group barrier for LDS hand-offs inside the chunk loop: waits for this wave's LDS
 // operations only. Global loads (the next chunk's prefetch) and stores (outputs, checkpoints)
@@ -312,21 +312,19 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
     //      F (times 2^(G_end(P) - G)), Kt/Qt (times 2^G); every factor is <= 1. Each thread sums
     //      the row-group totals in the same order, so G at a block's last row equals G_end. ------
     {
-      // Row-group sums in increasing order (unrolled, with a wave-uniform bound, so the loads
-      // issue back to back): gs = G before the block, pre = G before the thread's rows,
-      // gend = G at the block's last row.
-      f4 gs = {0.f, 0.f, 0.f, 0.f}, pre, gend;
+      // Row-group sums in increasing order: whole blocks before this one (a wave-uniform
+      // loop), then the four groups of this block. gs = G before the block, pre = G before
+      // the thread's rows, gend = G at the block's last row; every thread of a block adds the
+      // same terms in the same order, so G at a block's last row equals gend exactly.
+      f4 gs = {0.f, 0.f, 0.f, 0.f};
+      for (int mm = 0; mm < 4 * Pm; ++mm) gs += *reinterpret_cast<const f4*>(&L.u4.part[mm][c4]);
+      f4 blk[4];
 #pragma unroll
-      for (int mm = 0; mm < PC / 4; ++mm) {
-        if (mm == 4 * Pm) pre = gs;
-        if (mm == m4) gend = pre;
-        if (mm < 4 * Pm + 4) {
-          const f4 pv = *reinterpret_cast<const f4*>(&L.u4.part[mm][c4]);
-          if (mm < 4 * Pm) gs += pv;
-          else if (mm < m4) pre += pv;
-          else gend += pv;
-        }
-      }
+      for (int q = 0; q < 4; ++q) blk[q] = *reinterpret_cast<const f4*>(&L.u4.part[4 * Pm + q][c4]);
+      const int mq = m4 & 3;
+      const f4 s1 = gs + blk[0], s2 = s1 + blk[1], s3 = s2 + blk[2];
+      const f4 pre = mq == 0 ? gs : (mq == 1 ? s1 : (mq == 2 ? s2 : s3));
+      const f4 gend = s3 + blk[3];
       if ((m4 & 3) == 3) {
         *reinterpret_cast<f4*>(&L.ge[Pm][c4]) = gend;
         if (Pm == PNB - 1)
@@ -344,23 +342,22 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
                              __uint_as_float(kcur[i].y << 16), __uint_as_float(kcur[i].y & 0xffff0000u)};
         const float qr[4] = {__uint_as_float(qcur[i].x << 16), __uint_as_float(qcur[i].x & 0xffff0000u),
                              __uint_as_float(qcur[i].y << 16), __uint_as_float(qcur[i].y & 0xffff0000u)};
-        half4 hka, hqa, hkt, hqt, hf;
+        f4 ka, qa, kt, qt, fv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float G = pre[e] + Gl[i][e];
           const float e1 = fexp2(G - gs[e]);
-          const float ka = kr[e] * e1, qa = qr[e] * e1;
-          hka[e] = (_Float16)ka;
-          hqa[e] = (_Float16)qa;
-          hkt[e] = (_Float16)(ka * y[e]);
-          hqt[e] = (_Float16)(qa * y[e]);
-          hf[e] = (_Float16)(kr[e] * fexp2(gend[e] - G));
+          ka[e] = kr[e] * e1;
+          qa[e] = qr[e] * e1;
+          kt[e] = ka[e] * y[e];
+          qt[e] = qa[e] * y[e];
+          fv[e] = kr[e] * fexp2(gend[e] - G);
         }
-        *reinterpret_cast<half4*>(&L.u1.a.ka[r][c4]) = hka;
-        *reinterpret_cast<half4*>(&L.u1.a.qa[r][c4]) = hqa;
-        *reinterpret_cast<half4*>(&L.kt[r][c4]) = hkt;
-        *reinterpret_cast<half4*>(&L.qt[r][c4]) = hqt;
-        *reinterpret_cast<half4*>(&L.u3.f16[r][c4]) = hf;
+        *reinterpret_cast<half4*>(&L.u1.a.ka[r][c4]) = to_h4(ka);
+        *reinterpret_cast<half4*>(&L.u1.a.qa[r][c4]) = to_h4(qa);
+        *reinterpret_cast<half4*>(&L.kt[r][c4]) = to_h4(kt);
+        *reinterpret_cast<half4*>(&L.qt[r][c4]) = to_h4(qt);
+        *reinterpret_cast<half4*>(&L.u3.f16[r][c4]) = to_h4(fv);
       }
     }
     lds_barrier();
@@ -385,21 +382,18 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
         const int p = pi == 0 ? pa : pb;
         if (p < 0) break;
         const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
+        {   // this pair's column factor, two channels per lane (read back by this wave only)
+          const int i0 = 2 * l;
+          const float g0 = Pb > 0 ? L.ge[Pb - 1][i0] : 0.f, g1 = Pb > 0 ? L.ge[Pb - 1][i0 + 1] : 0.f;
+          L.xvh[p][i0] = (_Float16)fexp2(g0 - L.ge[Q][i0]);
+          L.xvh[p][i0 + 1] = (_Float16)fexp2(g1 - L.ge[Q][i0 + 1]);
+        }
         f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < PD / 32; ++kk) {
           const int c = 32 * kk + 8 * lq;
-          const half8 fk = ld8(&L.u3.f16[16 * Q + l16][c]);
-          float gsP[8], geQ[8];
-          if (Pb > 0) ld_f8(&L.ge[Pb - 1][c], gsP);
-          else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gsP[e] = 0.f;
-          }
-          ld_f8(&L.ge[Q][c], geQ);
-          half8 bb;   // k_s 2^(G_start(P) - G_s) = F_s 2^(G_start(P) - G_end(Q))
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bb[e] = (_Float16)((float)fk[e] * fexp2(gsP[e] - geQ[e]));
+          // k_s 2^(G_start(P) - G_s) = F_s 2^(G_start(P) - G_end(Q)), packed fp16 products
+          const half8 bb = ld8(&L.u3.f16[16 * Q + l16][c]) * ld8(&L.xvh[p][c]);
           akk = mfma32(ld8(&L.u1.a.ka[16 * Pb + l16][c]), bb, akk);
           aqk = mfma32(ld8(&L.u1.a.qa[16 * Pb + l16][c]), bb, aqk);
         }
@@ -411,39 +405,38 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
         }
       }
       if (w < PNB) {
-        if (l < 16) {   // column j of the inverse of the diagonal block w
-          const int Pb = w, j = l;
-          // lane j holds row j of the block; row r's entries are broadcast with readlane
-          float rowv[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f4 rr = *reinterpret_cast<const f4*>(&L.u2.l32[16 * Pb + j][16 * Pb + 4 * q4]);
-            rowv[4 * q4] = rr[0]; rowv[4 * q4 + 1] = rr[1]; rowv[4 * q4 + 2] = rr[2]; rowv[4 * q4 + 3] = rr[3];
-          }
-          float x[16];
+        {   // inverse of the diagonal block w by forward substitution. Column j = l / 4 runs on
+            // four lanes; lane q = l % 4 keeps x_s for s = q (mod 4) in xs[s / 4] and sums
+            // those terms (the block stores zeros on and above its diagonal, and xs starts at 0,
+            // so not-yet-computed terms add nothing); a butterfly gives all four lanes the sum.
+          const int Pb = w, j = l >> 2, q = l & 3;
+          float x[16], xs[4] = {0.f, 0.f, 0.f, 0.f};
           x[0] = j == 0 ? 1.f : 0.f;
+          if (q == 0) xs[0] = x[0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) {
-            // x_r = [r == j] - sum_{s<r} L_rs x_s, as four interleaved partial sums
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float part = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) {
-              const float lrs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rowv[s]), r));
-              acc[s & 3] = __builtin_fmaf(lrs, x[s], acc[s & 3]);
-            }
-            x[r] = (r == j ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            for (int k = 0; k <= (r - 1) / 4; ++k)
+              part = __builtin_fmaf(L.u2.l32[16 * Pb + r][16 * Pb + 4 * k + q], xs[k], part);
+            float tot = part + __shfl_xor(part, 1);
+            tot = tot + __shfl_xor(tot, 2);
+            x[r] = (r == j ? 1.f : 0.f) - tot;
+            if ((r & 3) == q) xs[r >> 2] = x[r];
           }
+          if (q == 0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) L.u4.nd[16 * Pb + r][j] = x[r];
+            for (int r = 0; r < 16; ++r) L.u4.nd[16 * Pb + r][j] = x[r];
+          }
         }
       } else if (w >= PNB + 2) {   // Kbar^T = (F * zv)^T
         for (int it = t - (PNB + 2) * 64; it < PD * (PC / 8); it += (PNW - PNB - 2) * 64) {
           const int i = it % PD, s0 = (it / PD) * 8, Q = s0 >> 4;
-          const float z = fexp2(L.ge[PNB - 1][i] - L.ge[Q][i]);
-          half8 kb;
+          const _Float16 z = (_Float16)fexp2(L.ge[PNB - 1][i] - L.ge[Q][i]);
+          half8 fk;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kb[e] = (_Float16)((float)L.u3.f16[s0 + e][i] * z);
-          *reinterpret_cast<half8*>(&L.kbt[i][s0]) = kb;
+          for (int e = 0; e < 8; ++e) fk[e] = L.u3.f16[s0 + e][i];
+          *reinterpret_cast<half8*>(&L.kbt[i][s0]) = fk * z;
         }
       }
     }
