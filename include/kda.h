@@ -115,7 +115,13 @@ kda_status kda_slot_checkpoint(kda_pool* pool, int32_t src, int32_t dst, void* s
  * chunk must be the instantiated chunk for dk; ckpt_interval a multiple of chunk.
  * Every h_* array is a host copy of the matching d_* device array (same contents); the host
  * copies drive validation, the device copies drive the kernels. Zero-length sequences are
- * allowed. The workspace is unused in this build (workspace_bytes may be 0).               */
+ * allowed.
+ * workspace: device memory, 256-byte aligned, of at least kda_prefill_workspace_bytes(pool,
+ * n_tok, n_seq, chunk) bytes, owned by the caller and not touched by anything else until the
+ * work on `stream` is done (the chunked form stages every chunk's S-independent operands there,
+ * 65 KiB per chunk and head). NULL: the pool allocates its own buffer on first use and grows it
+ * with hipMalloc (after a device synchronize) when a larger prefill comes; it is freed by
+ * kda_pool_destroy. A workspace smaller than the need returns KDA_EWORKSPACE.            */
 typedef struct {
   const void* q; const void* k; const void* v;   /* bf16 */
   const float* a; const float* b;
@@ -127,6 +133,9 @@ typedef struct {
   const int32_t* h_ckpt_slot;  const int32_t* d_ckpt_slot;    /* concat, or NULL        */
   void* workspace; size_t workspace_bytes;
 } kda_prefill_args;
+/* Workspace bytes that any prefill of n_tok tokens in n_seq sequences needs (an upper bound
+ * over length mixes: at most floor(n_tok / chunk) + n_seq chunks); 0 where the token-by-token
+ * kernel runs (dk = 16) or for n_seq <= 0.                                                 */
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
                                    int32_t chunk);
 kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);

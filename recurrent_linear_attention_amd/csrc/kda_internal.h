@@ -35,6 +35,8 @@ struct PrefillLaunch {
   const int32_t* out_slot;     // device
   const int32_t* ckpt_slot;    // device or nullptr
   int32_t max_len;             // longest sequence (host-known), sizes the grid
+  int64_t n_chunks;            // sum over sequences of ceil(len / chunk) (host-known)
+  void* workspace;             // device, at least prefill_workspace_bytes(...) bytes
 };
 
 hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B,
@@ -49,6 +51,9 @@ hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s);
 hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t s);
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
+// Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
+// shapes that run the token-by-token kernel).
+size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);
 // Token-by-token prefill with the decode step (reference-form kernel; any supported d).
 hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
 

@@ -64,6 +64,8 @@ struct kda_pool {
   std::vector<uint8_t> slot_state;     // SLOT_FREE / SLOT_IDLE / SLOT_PENDING
   std::vector<uint32_t> stamp;         // distinctness checks
   uint32_t epoch = 0;
+  void* ws = nullptr;                  // prefill workspace used when the caller passes none
+  size_t ws_bytes = 0;
 
   // Mark-and-check: returns false if a slot repeats within one validation pass.
   void begin_pass() {
@@ -185,6 +187,10 @@ kda_status kda_pool_create(const kda_pool_desc* d, void* state, void* ring, void
 
 kda_status kda_pool_destroy(kda_pool* p) {
   if (!p) return fail(KDA_EINVAL, "null pool");
+  if (p->ws) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p->ws);
+  }
   delete p;
   return KDA_OK;
 }
@@ -234,12 +240,14 @@ kda_status kda_slot_checkpoint(kda_pool* p, int32_t src, int32_t dst, void* stre
 
 size_t kda_prefill_workspace_bytes(const kda_pool* p, int32_t n_tok, int32_t n_seq,
                                    int32_t chunk) {
-  (void)p; (void)n_tok; (void)n_seq; (void)chunk;
-  return 0;
+  if (!p || n_tok < 0 || n_seq <= 0 || chunk <= 0) return 0;
+  // sum_i ceil(len_i / chunk) <= floor(n_tok / chunk) + n_seq
+  return kda::prefill_workspace_bytes(p->desc.dk, chunk, p->desc.num_heads, n_seq,
+                                      (int64_t)(n_tok / chunk) + n_seq);
 }
 
 static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool tensors_needed,
-                                   int32_t* max_len) {
+                                   int32_t* max_len, int64_t* n_chunks) {
   if (!p || !a) return fail(KDA_EINVAL, "null argument");
   if (a->n_seq < 0 || a->n_tok < 0) return fail(KDA_EINVAL, "negative n_seq / n_tok");
   if (a->chunk != kda::prefill_chunk_for(p->desc.dk))
@@ -248,6 +256,7 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
   if (a->ckpt_interval < 0 || (a->ckpt_interval > 0 && a->ckpt_interval % a->chunk != 0))
     return fail(KDA_EUNSUPPORTED, "checkpoint interval %d must be a multiple of chunk %d",
                 a->ckpt_interval, a->chunk);
+  *n_chunks = 0;
   if (a->n_seq == 0) {
     *max_len = 0;
     return a->n_tok == 0 ? KDA_OK : fail(KDA_EINVAL, "tokens without sequences");
@@ -262,12 +271,13 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
     return fail(KDA_EINVAL, "init_slot host and device copies must both be given or both NULL");
   const int32_t* cu = a->h_cu_seqlens;
   if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] must be 0");
-  int64_t n_ckpt = 0;
+  int64_t n_ckpt = 0, nch = 0;
   int32_t mx = 0;
   for (int32_t i = 0; i < a->n_seq; ++i) {
     if (cu[i + 1] < cu[i]) return fail(KDA_EINVAL, "cu_seqlens must be non-decreasing");
     int32_t len = cu[i + 1] - cu[i];
     mx = len > mx ? len : mx;
+    nch += (len + a->chunk - 1) / a->chunk;
     if (a->ckpt_interval > 0) n_ckpt += len / a->ckpt_interval;
   }
   if (cu[a->n_seq] != a->n_tok) return fail(KDA_EINVAL, "cu_seqlens[n_seq] != n_tok");
@@ -293,17 +303,57 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
     }
   }
   *max_len = mx;
+  *n_chunks = nch;
+  return KDA_OK;
+}
+
+// Device workspace of a prefill: the caller's buffer, checked against the need, or (when the
+// caller passes none) the pool's own buffer, grown on demand.
+static kda_status prefill_workspace(kda_pool* p, const kda_prefill_args* a, int64_t n_chunks,
+                                    void** ws) {
+  const size_t need =
+      kda::prefill_workspace_bytes(p->desc.dk, a->chunk, p->desc.num_heads, a->n_seq, n_chunks);
+  *ws = nullptr;
+  if (need == 0) return KDA_OK;
+  if (a->workspace) {
+    if (a->workspace_bytes < need)
+      return fail(KDA_EWORKSPACE, "workspace of %zu bytes, this prefill needs %zu",
+                  a->workspace_bytes, need);
+    if (!aligned(a->workspace, 256)) return fail(KDA_EINVAL, "workspace must be 256-byte aligned");
+    *ws = a->workspace;
+    return KDA_OK;
+  }
+  if (p->ws_bytes < need) {
+    if (p->ws) {
+      hipError_t e = hipDeviceSynchronize();   // earlier prefills may still read the old buffer
+      if (e != hipSuccess) return hip_fail(e, "workspace grow");
+      (void)hipFree(p->ws);
+      p->ws = nullptr;
+      p->ws_bytes = 0;
+    }
+    hipError_t e = hipMalloc(&p->ws, need);
+    if (e != hipSuccess) {
+      p->ws = nullptr;
+      return hip_fail(e, "workspace allocation");
+    }
+    p->ws_bytes = need;
+  }
+  *ws = p->ws;
   return KDA_OK;
 }
 
 kda_status kda_prefill(kda_pool* p, const kda_prefill_args* a, void* stream) {
   int32_t max_len = 0;
-  kda_status st = validate_prefill(p, a, true, &max_len);
+  int64_t n_chunks = 0;
+  kda_status st = validate_prefill(p, a, true, &max_len, &n_chunks);
   if (st != KDA_OK) return st;
   if (a->n_seq == 0) return KDA_OK;
+  void* ws = nullptr;
+  st = prefill_workspace(p, a, n_chunks, &ws);
+  if (st != KDA_OK) return st;
   kda::PrefillLaunch L{tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->n_seq, a->n_tok,
                        a->chunk, a->ckpt_interval, a->d_cu_seqlens, a->d_init_slot,
-                       a->d_out_slot, a->d_ckpt_slot, max_len};
+                       a->d_out_slot, a->d_ckpt_slot, max_len, n_chunks, ws};
   hipError_t e = kda::launch_prefill(p->view, L, as_stream(stream));
   return e == hipSuccess ? KDA_OK : hip_fail(e, "prefill launch");
 }
@@ -376,7 +426,8 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   kda_prefill_args pre = m->prefill;
   pre.q = m->q; pre.k = m->k; pre.v = m->v; pre.a = m->a; pre.b = m->b; pre.o = m->o;
   int32_t max_len = 0;
-  st = validate_prefill(p, &pre, false, &max_len);
+  int64_t n_chunks = 0;
+  st = validate_prefill(p, &pre, false, &max_len, &n_chunks);
   if (st != KDA_OK) return st;
   // Decode and verify slots: idle, distinct from each other and from the prefill's slots.
   p->begin_pass();
@@ -407,9 +458,12 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   };
   hipError_t e = hipSuccess;
   if (pre.n_seq > 0) {
+    void* ws = nullptr;
+    st = prefill_workspace(p, &pre, n_chunks, &ws);
+    if (st != KDA_OK) return st;
     kda::PrefillLaunch L{part(0), pre.n_seq, pre.n_tok, pre.chunk, pre.ckpt_interval,
                          pre.d_cu_seqlens, pre.d_init_slot, pre.d_out_slot, pre.d_ckpt_slot,
-                         max_len};
+                         max_len, n_chunks, ws};
     e = kda::launch_prefill(p->view, L, s);
     if (e != hipSuccess) return hip_fail(e, "mixed: prefill launch");
   }

@@ -13,22 +13,25 @@
 //     S' = Diag(2^(G_C)) S + Kbar^T W,    Kbar_s = k_s 2^(G_C - G_s)
 // Derivation: write each step as S_r = Diag(a_r) S_{r-1} + k_r w_r^T and unroll over the chunk.
 //
-// Design for MI355X:
-//   * one work-group (8 waves, two per SIMD) per (sequence, head, slice of VS value columns).
-//     Value columns of S evolve independently, so slices need no exchange; the launcher picks
-//     VS in {16, 32, 64, 128} so that sequences x heads x slices stays within two rounds of
-//     CUs (a lone 8192-token prompt at 32 heads runs 8 slices per head, a batch of 6 prompts
-//     2 slices), and work-groups start longest sequence first. The S-independent part
-//     (A_kk, A_qk, T) is recomputed per slice.
-//   * all contractions run on v_mfma_f32_16x16x32_f16 / 16x16x16f16 with fp32 accumulation.
-//     fp16 operands (same rate as bf16, 3 more mantissa bits) keep the chunked form within
-//     2e-3 of the sequential fp64 result; bf16 operands do not (5e-3 in emulation). The state
-//     stays fp32 in MFMA accumulator registers across chunks; only operand copies are fp16.
-//   * every exponential factor is at most 1 except the column factor of the diagonal 16x16
-//     blocks of A_kk / A_qk, bounded by the 16-token decay of the block; beyond 2^14 on any
-//     channel the kernel flags KDA_DEVERR_DECAY_RANGE.
-//   * the next chunk's q/k/a/v/b are loaded into registers while the current chunk computes.
-//   * block ids are mapped so that all slices of one head run on the same XCD and share its L2.
+// Design for MI355X: everything that does not depend on S (decays, Kt, Qt, Kbar, A_qk, T,
+// 2^(G_C)) is computed for every (chunk, head) at once by chunk_prep_kernel, which fills the
+// GPU whatever the batch shape; the sequential part left for state_pass_kernel is three
+// small matrix products per chunk (X, W, then O and S'), so the per-chunk latency of a long
+// sequence is a few hundred MFMA cycles instead of the whole chunk computation.
+//   * chunk_prep_kernel writes each chunk's operands as fp16 16x32 A-operand fragments of
+//     v_mfma_f32_16x16x32_f16 in lane order (one 1 KiB fragment = 64 lanes x 16 bytes), so the
+//     state pass copies a chunk's 64.5 KiB block into LDS with coalesced 16-byte loads and
+//     reads every fragment with one conflict-free ds_read_b128 per lane.
+//   * state_pass_kernel keeps the state S in fp32 MFMA accumulators for the whole sequence.
+//     The accumulator tiles of S, X and W become B operands of the next product in registers:
+//     fp16 conversion plus two lane-half swaps (v_permlane32_swap, v_permlane16_swap) per
+//     pair of 16-row tiles; no LDS round trip and no barrier inside the chain.
+//   * fp16 operands (same rate as bf16, 3 more mantissa bits) keep the chunked form within
+//     2e-3 of the sequential fp64 result; bf16 operands do not (5e-3 in emulation).
+//   * decay factors are products of a over row ranges inside a chunk, formed by
+//     multiplication: every factor is at most 1 except the column factor of the diagonal
+//     16x16 blocks of A_kk / A_qk, the inverse of the block's 16-token decay; a block decay
+//     below 2^-14 on any channel is flagged as KDA_DEVERR_DECAY_RANGE.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -40,51 +43,32 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 constexpr int PD = 128;           // head dim (dk = dv)
 constexpr int PC = 64;            // chunk
 constexpr int PNB = PC / 16;      // 16-row blocks per chunk
-constexpr int PNW = 8;            // waves per work-group
-constexpr int PNT = 64 * PNW;
-constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
-constexpr int PG = PD + 4;        // row pitch (floats) of the G array (16-row fragment reads hit
-                                  // every LDS bank exactly four times)
-constexpr int PC16 = PC + 8;      // row pitch (halves) of [.][PC] fp16 arrays
-constexpr int PL = PC + 8;        // row pitch (floats) of the fp32 [PC][PC] array
 constexpr int NPAIR = PNB * (PNB + 1) / 2;
-constexpr float DIAG_LOG2_LIMIT = 14.f;
+constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
+constexpr int PC16 = PC + 8;      // row pitch (halves) of [.][PC] fp16 arrays
+constexpr float DIAG_DECAY_MIN = 1.f / 16384.f;   // 2^-14
 
-template <int VS>
-struct PfLds {
-  _Float16 kt[PC][P16];      // Kt = k 2^G (fp16)
-  _Float16 qt[PC][P16];      // Qt = q 2^G (fp16)
-  union {
-    struct {                 // A-operands of A_kk / A_qk: rows of block P times 2^(G - G_start(P))
-      _Float16 ka[PC][P16];
-      _Float16 qa[PC][P16];
-    } a;
-    _Float16 s16t[VS][P16];  // S^T (fp16 operand copy)
-  } u1;
-  _Float16 kbt[PD][PC16];    // Kbar^T
-  union {
-    float l32[PC][PL];       // Diag(b) A_kk, strictly lower
-    _Float16 x16t[VS][PC16]; // X^T
-  } u2;
-  union {
-    _Float16 f16[PC][P16];   // F_s = k_s 2^(G_end(block of s) - G_s)
-    _Float16 w16t[VS][PC16]; // W^T
-  } u3;
-  _Float16 aqk[PC][PC16];    // A_qk, zero above the diagonal
-  _Float16 t16[PC][PC16];    // T, zero above the diagonal
-  union {
-    float part[PC / 4][PD];  // sums of log2 a over each group of 4 rows
-    float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
-  } u4;
-  float ge[PNB][PD];         // G at the last row of each block
-  _Float16 xvh[NPAIR][PD];   // 2^(G_start(P) - G_end(Q)) per pair, fp16
-  float gam[PD];             // 2^(G_C)
-  float b[PC];
-};
+// ---- per-(chunk, head) operand block --------------------------------------------------------
+// A fragment holds a 16 x 32 fp16 tile A[16][32] as the A operand of v_mfma_f32_16x16x32_f16:
+// lane L = l16 + 16 * lq owns A[l16][8 lq .. 8 lq + 7] at bytes 16 L .. 16 L + 15.
+constexpr int FRAG = 1024;
+constexpr int OFF_KT = 0;             // Kt:     f = 4 rt + kk  (token tile rt, channel block kk)
+constexpr int OFF_QT = 16 * FRAG;     // Qt:     same
+constexpr int OFF_KB = 32 * FRAG;     // Kbar^T: f = 2 rt + kk  (channel tile rt < 8, token block kk)
+constexpr int OFF_T = 48 * FRAG;      // T:      f = 2 rt + kk  (token tile rt, token block kk <= rt/2)
+constexpr int OFF_AQ = 56 * FRAG;     // A_qk:   same
+constexpr int OFF_GAM = 64 * FRAG;    // 2^(G_C), fp32 [PD]
+constexpr int BLOCK_USED = 64 * FRAG + 4 * PD;
+constexpr int BLOCK_BYTES = 65 * FRAG;
+
+__device__ __forceinline__ int frag_lane_byte(int row, int k) {   // byte of A[row][k] in its fragment
+  return ((row & 15) + 16 * ((k & 31) >> 3)) * 16 + (k & 7) * 2;
+}
 
 __device__ __forceinline__ f4 mfma32(half8 a, half8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -92,51 +76,113 @@ __device__ __forceinline__ f4 mfma32(half8 a, half8 b, f4 c) {
 __device__ __forceinline__ f4 mfma16(half4 a, half4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
-// Decay factors use the hardware exp2 / log2 (the fast path of HIP's math library): a result
-// below 2^-126 flushes to zero, which only drops contributions already below fp32 resolution.
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float flog2(float x) { return __log2f(x); }
-
 __device__ __forceinline__ half8 ld8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
-__device__ __forceinline__ void ld_f8(const float* p, float (&f)[8]) {
-  f4 x = *reinterpret_cast<const f4*>(p), y = *reinterpret_cast<const f4*>(p + 4);
-  f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3]; f[4] = y[0]; f[5] = y[1]; f[6] = y[2]; f[7] = y[3];
-}
-__device__ __forceinline__ void unpack8(const _Float16* raw, float (&f)[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(raw);
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __uint_as_float(ws[e] << 16);
-    f[2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
-  }
-}
 // fp32 -> fp16 (round to nearest even) as packed conversions (v_cvt_pk_f16_f32)
 __device__ __forceinline__ half4 to_h4(f4 x) { return __builtin_convertvector(x, half4); }
 
-// Work-group barrier for LDS hand-offs inside the chunk loop: waits for this wave's LDS
-// operations only. Global loads (the next chunk's prefetch) and stores (outputs, checkpoints)
-// stay in flight across it; no wave of the work-group reads what another wave stores to global
-// memory in the loop, and the loop never reads a register before its load has been waited on.
+// Work-group barrier for LDS hand-offs: waits for this wave's LDS operations only; global
+// loads and stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Index of the sequence with the given rank in descending length order (ties: lower index
-// first). Uniform across the work-group; O(n_seq^2), used once per work-group.
-__device__ __forceinline__ int seq_by_rank(const int32_t* cu, int n_seq, int rank) {
-  if (n_seq > 256) return rank;
-  for (int j = 0; j < n_seq; ++j) {
-    const int lj = cu[j + 1] - cu[j];
+// Lane exchanges inside groups of four lanes (DPP quad_perm: a VALU operand modifier, no
+// LDS round trip): value of lane l ^ 1 and of lane l ^ 2.
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// Raw buffer resource over [base, base + bytes): loads beyond return 0, stores beyond are
+// dropped by the hardware, so ragged chunk tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---- plan: chunk offsets, checkpoint offsets and the longest-first order -----------------
+// choff[i] = sum_{j<i} ceil(len_j / PC) (n_seq + 1 entries), ckoff[i] = sum_{j<i} floor(len_j /
+// ckpt_interval), order[rank] = index of the sequence with that rank in descending length
+// (ties: lower index first).
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_MAX_SORT = 8192;
+
+__global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_t* __restrict__ cu,
+                                                                  int n_seq, int ckpt_interval,
+                                                                  int32_t* __restrict__ choff,
+                                                                  int32_t* __restrict__ ckoff,
+                                                                  int32_t* __restrict__ order) {
+  __shared__ int32_t len_s[PLAN_MAX_SORT];
+  __shared__ int32_t part_c[PLAN_THREADS], part_k[PLAN_THREADS];
+  const int t = threadIdx.x;
+  const int per = (n_seq + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int j0 = t * per, j1 = min(n_seq, j0 + per);
+  int sc = 0, sk = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int len = cu[j + 1] - cu[j];
+    sc += (len + PC - 1) / PC;
+    sk += ckpt_interval > 0 ? len / ckpt_interval : 0;
+  }
+  part_c[t] = sc;
+  part_k[t] = sk;
+  __syncthreads();
+  if (t == 0) {   // exclusive scan of the per-thread sums (1024 entries, once per launch)
+    int ac = 0, ak = 0;
+    for (int i = 0; i < PLAN_THREADS; ++i) {
+      const int c = part_c[i], k = part_k[i];
+      part_c[i] = ac;
+      part_k[i] = ak;
+      ac += c;
+      ak += k;
+    }
+    choff[n_seq] = ac;
+  }
+  __syncthreads();
+  sc = part_c[t];
+  sk = part_k[t];
+  for (int j = j0; j < j1; ++j) {
+    const int len = cu[j + 1] - cu[j];
+    choff[j] = sc;
+    ckoff[j] = sk;
+    sc += (len + PC - 1) / PC;
+    sk += ckpt_interval > 0 ? len / ckpt_interval : 0;
+  }
+  if (n_seq > PLAN_MAX_SORT) {
+    for (int j = t; j < n_seq; j += PLAN_THREADS) order[j] = j;
+    return;
+  }
+  for (int j = t; j < n_seq; j += PLAN_THREADS) len_s[j] = cu[j + 1] - cu[j];
+  __syncthreads();
+  for (int j = t; j < n_seq; j += PLAN_THREADS) {
+    const int lj = len_s[j];
     int rj = 0;
     for (int k = 0; k < n_seq; ++k) {
-      const int lk = cu[k + 1] - cu[k];
+      const int lk = len_s[k];
       rj += (lk > lj) || (lk == lj && k < j);
     }
-    if (rj == rank) return j;
+    order[rj] = j;
   }
-  return rank;
 }
+
+// ---- chunk_prep_kernel: the S-independent part of one (chunk, head) -------------------------
+constexpr int PNW = 8;            // waves per work-group
+constexpr int PNT = 64 * PNW;
+
+struct PrepLds {
+  _Float16 ka[PC][P16];      // rows of block P times 2^(G - G_start(P))     (A operand, A_kk)
+  _Float16 qa[PC][P16];      // q likewise                                   (A operand, A_qk)
+  _Float16 f16[PC][P16];     // F_s = k_s 2^(G_end(block of s) - G_s)
+  float ldg[PNB][16][16];    // diagonal blocks of Diag(b) A_kk (strictly lower), fp32
+  _Float16 loff[PC][PC16];   // Diag(b) A_kk below the diagonal blocks, fp16
+  union {
+    float part[PC / 4][PD];  // products of a over each group of 4 rows
+    float nd[PC][16];        // diagonal 16x16 blocks of (I + Diag(b) A_kk)^-1
+  } u4;
+  float bp[PNB][PD];         // decay over each block: 2^(G_end(P) - G_start(P))
+  _Float16 xvh[NPAIR][PD];   // 2^(G_start(P) - G_end(Q)) per pair, fp16
+  float b[PC];
+};
 
 // pair index p = P(P+1)/2 + Q for Q <= P
 __device__ __forceinline__ int pair_p(int p) { return p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0)); }
@@ -144,404 +190,508 @@ __device__ __forceinline__ int pair_p(int p) { return p >= 6 ? 3 : (p >= 3 ? 2 :
 // Column block Q of T = N Diag(b), N = (I + Diag(b) A_kk)^-1, from the diagonal inverses:
 // N_PQ = -N_PP sum_{Q<=R<P} L_PR N_RQ, 16x16x16 fp16 products with fp32 accumulation. The
 // accumulator layout of a 16x16x16 product equals its B-operand layout, so N_RQ stays in
-// registers from one product to the next.
-template <int Q, class Lds>
-__device__ __forceinline__ void t_column(Lds& L, int l16, int lq) {
+// registers from one product to the next. T blocks go straight to their fragments.
+template <int Q>
+__device__ __forceinline__ void t_column(const PrepLds& L, char* blk, int l16, int lq) {
   f4 nq[PNB];
 #pragma unroll
   for (int e = 0; e < 4; ++e) nq[Q][e] = L.u4.nd[16 * Q + 4 * lq + e][l16];
   const float bq = L.b[16 * Q + l16];
+  auto put = [&](int Pb, const f4& v) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) L.t16[16 * Q + 4 * lq + e][16 * Q + l16] = (_Float16)(nq[Q][e] * bq);
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * Pb + 4 * lq + e, col = 16 * Q + l16;
+      *reinterpret_cast<_Float16*>(blk + OFF_T + (2 * Pb + (col >> 5)) * FRAG + frag_lane_byte(row, col)) =
+          (_Float16)(v[e] * bq);
+    }
+  };
+  put(Q, nq[Q]);
 #pragma unroll
   for (int Pb = Q + 1; Pb < PNB; ++Pb) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int R = Q; R < Pb; ++R) {
-      const f4 lr = *reinterpret_cast<const f4*>(&L.u2.l32[16 * Pb + l16][16 * R + 4 * lq]);
-      acc = mfma16(to_h4(lr), to_h4(nq[R]), acc);
+      const half4 lr = *reinterpret_cast<const half4*>(&L.loff[16 * Pb + l16][16 * R + 4 * lq]);
+      acc = mfma16(lr, to_h4(nq[R]), acc);
     }
     const f4 np = *reinterpret_cast<const f4*>(&L.u4.nd[16 * Pb + l16][4 * lq]);
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
     nq[Pb] = -mfma16(to_h4(np), to_h4(acc), zero);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) L.t16[16 * Pb + 4 * lq + e][16 * Q + l16] = (_Float16)(nq[Pb][e] * bq);
+    put(Pb, nq[Pb]);
   }
 }
 
-// Raw inputs of one chunk, held in registers between chunks (prefetch). Thread t owns key
-// rows 4m .. 4m+3 (m = t / 32) and key channels 4cq .. 4cq+3 (cq = t % 32): a row of 32
-// threads reads 256 contiguous bytes of q / k and 512 of a.
-template <int VS>
-struct Stage {
-  static constexpr int NCT = VS / 16;
-  static constexpr int NXT = (4 * NCT + PNW - 1) / PNW;   // X tiles per wave
-  uint2 k[4], q[4];       // 4 bf16 each
-  float4 a[4];
-  uint32_t v[NXT][4];     // V of the wave's X tiles: bf16 bits, rows 4*lq+e (kept unpacked so
-                          // that nothing waits on these loads before the next chunk)
-  float b;
+// One work-group per (chunk, head): blockIdx.x = global chunk index * H + head. Thread t
+// owns key rows 4m .. 4m+3 (m = t / 32) and key channels 4cq .. 4cq+3 (cq = t % 32) in the
+// staging and operand phases.
+__global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillLaunch A,
+                                                            const int32_t* __restrict__ choff,
+                                                            char* __restrict__ blocks) {
+  __shared__ PrepLds L;
+  const int H = P.H, h = blockIdx.x % H, gc = blockIdx.x / H;
+  // sequence of this chunk: the last i with choff[i] <= gc (binary search, uniform)
+  int lo_i = 0, hi_i = A.n_seq - 1;
+  while (lo_i < hi_i) {
+    const int mid = (lo_i + hi_i + 1) >> 1;
+    if (choff[mid] <= gc) lo_i = mid; else hi_i = mid - 1;
+  }
+  const int si = lo_i, c = gc - choff[si];
+  const int tok0 = A.cu_seqlens[si] + PC * c;
+  const int n = min(PC, A.cu_seqlens[si + 1] - tok0);
+  char* blk = blocks + (size_t)blockIdx.x * BLOCK_BYTES;
+  const size_t hstride = (size_t)H * PD;
+
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, l16 = l & 15, lq = l >> 4;
+  const int m4 = t >> 5, c4 = (t & 31) * 4, Pm = m4 >> 2, mq = m4 & 3;
+
+  // ---- raw rows; padded rows (r >= n) have k = q = 0, a = 1, b = 0 ---------------------------
+  uint2 kr4[4], qr4[4];
+  f4 cpre[4], dsuf[3];   // cpre[i] = a_0..a_i, dsuf[i] = a_{i+1}..a_3 over the thread's rows
+  {
+    f4 av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * m4 + i;
+      uint2 kk = make_uint2(0, 0), qq = make_uint2(0, 0);
+      float4 a = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (r < n) {
+        const size_t off = (size_t)(tok0 + r) * hstride + (size_t)h * PD + c4;
+        kk = *reinterpret_cast<const uint2*>(A.t.k + off);
+        qq = *reinterpret_cast<const uint2*>(A.t.q + off);
+        a = *reinterpret_cast<const float4*>(A.t.a + off);
+      }
+      kr4[i] = kk;
+      qr4[i] = qq;
+      av[i] = f4{a.x, a.y, a.z, a.w};
+    }
+    cpre[0] = av[0];
+    cpre[1] = cpre[0] * av[1];
+    cpre[2] = cpre[1] * av[2];
+    cpre[3] = cpre[2] * av[3];
+    dsuf[2] = av[3];
+    dsuf[1] = av[2] * av[3];
+    dsuf[0] = av[1] * dsuf[1];
+    *reinterpret_cast<f4*>(&L.u4.part[m4][c4]) = cpre[3];
+  }
+  if (t < PC) L.b[t] = t < n ? A.t.b[(size_t)(tok0 + t) * H + h] : 0.f;
+  __syncthreads();
+
+  // ---- decayed fp16 operands: Ka/Qa (rows of block P times 2^(G - G_start(P))), F (times
+  //      2^(G_end(P) - G)) to LDS; Kt/Qt (times 2^G) straight to their fragments. Every
+  //      factor is at most 1. ---------------------------------------------------------------
+  {
+    // Products of the row-group decays: gsp over the blocks before this one (a wave-uniform
+    // loop), then the four groups of this block: pre before the thread's rows, post after.
+    f4 gsp = {1.f, 1.f, 1.f, 1.f};
+    for (int mm = 0; mm < 4 * Pm; ++mm) gsp *= *reinterpret_cast<const f4*>(&L.u4.part[mm][c4]);
+    f4 blk4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) blk4[q] = *reinterpret_cast<const f4*>(&L.u4.part[4 * Pm + q][c4]);
+    const f4 one = {1.f, 1.f, 1.f, 1.f};
+    const f4 p01 = blk4[0] * blk4[1], p23 = blk4[2] * blk4[3];
+    const f4 pre = mq == 0 ? one : (mq == 1 ? blk4[0] : (mq == 2 ? p01 : p01 * blk4[2]));
+    const f4 post = mq == 3 ? one : (mq == 2 ? blk4[3] : (mq == 1 ? p23 : blk4[1] * p23));
+    if (mq == 3) {
+      const f4 bpv = p01 * p23;   // decay over the whole block
+      *reinterpret_cast<f4*>(&L.bp[Pm][c4]) = bpv;
+      if (Pm == PNB - 1) *reinterpret_cast<f4*>(blk + OFF_GAM + 4 * c4) = gsp * bpv;
+      if (bpv[0] < DIAG_DECAY_MIN || bpv[1] < DIAG_DECAY_MIN || bpv[2] < DIAG_DECAY_MIN ||
+          bpv[3] < DIAG_DECAY_MIN)
+        atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * m4 + i;
+      const float kr[4] = {__uint_as_float(kr4[i].x << 16), __uint_as_float(kr4[i].x & 0xffff0000u),
+                           __uint_as_float(kr4[i].y << 16), __uint_as_float(kr4[i].y & 0xffff0000u)};
+      const float qr[4] = {__uint_as_float(qr4[i].x << 16), __uint_as_float(qr4[i].x & 0xffff0000u),
+                           __uint_as_float(qr4[i].y << 16), __uint_as_float(qr4[i].y & 0xffff0000u)};
+      const f4 e1 = pre * cpre[i];                                   // 2^(G_r - G_start(P))
+      const f4 e2 = i == 3 ? post : post * dsuf[i < 3 ? i : 0];     // 2^(G_end(P) - G_r)
+      f4 ka, qa, kt, qt, fv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ka[e] = kr[e] * e1[e];
+        qa[e] = qr[e] * e1[e];
+        kt[e] = ka[e] * gsp[e];
+        qt[e] = qa[e] * gsp[e];
+        fv[e] = kr[e] * e2[e];
+      }
+      *reinterpret_cast<half4*>(&L.ka[r][c4]) = to_h4(ka);
+      *reinterpret_cast<half4*>(&L.qa[r][c4]) = to_h4(qa);
+      *reinterpret_cast<half4*>(&L.f16[r][c4]) = to_h4(fv);
+      const int fo = (4 * (r >> 4) + (c4 >> 5)) * FRAG + frag_lane_byte(r, c4);
+      *reinterpret_cast<half4*>(blk + OFF_KT + fo) = to_h4(kt);
+      *reinterpret_cast<half4*>(blk + OFF_QT + fo) = to_h4(qt);
+    }
+  }
+  __syncthreads();
+
+  // ---- A_kk, A_qk block pairs on matrix cores. Waves 0-3: diagonal pair (w, w), then the
+  //      inverse of that block by forward substitution (the wave's own LDS writes, no barrier
+  //      needed). Waves 4-7: the six off-diagonal pairs; waves 6-7 also Kbar^T and the zero
+  //      blocks above the diagonal inside the T / A_qk fragments. ---------------------------
+  {
+    int pa, pb;
+    switch (w) {
+      case 0: pa = 0; pb = -1; break;
+      case 1: pa = 2; pb = -1; break;
+      case 2: pa = 5; pb = -1; break;
+      case 3: pa = 9; pb = -1; break;
+      case 4: pa = 1; pb = 7; break;
+      case 5: pa = 3; pb = 8; break;
+      case 6: pa = 4; pb = -1; break;
+      default: pa = 6; pb = -1; break;
+    }
+    for (int pi = 0; pi < 2; ++pi) {
+      const int p = pi == 0 ? pa : pb;
+      if (p < 0) break;
+      const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
+      {   // this pair's column factor, two channels per lane (read back by this wave only):
+          // the decay between the end of block Q and the start of block P, or the inverse
+          // decay of the block when P = Q
+        const int i0 = 2 * l;
+        float z0, z1;
+        if (Pb == Q) {
+          z0 = __builtin_amdgcn_rcpf(L.bp[Q][i0]);
+          z1 = __builtin_amdgcn_rcpf(L.bp[Q][i0 + 1]);
+        } else {
+          z0 = 1.f;
+          z1 = 1.f;
+          for (int R = Q + 1; R < Pb; ++R) {
+            z0 *= L.bp[R][i0];
+            z1 *= L.bp[R][i0 + 1];
+          }
+        }
+        L.xvh[p][i0] = (_Float16)z0;
+        L.xvh[p][i0 + 1] = (_Float16)z1;
+      }
+      f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < PD / 32; ++kk) {
+        const int c = 32 * kk + 8 * lq;
+        // k_s 2^(G_start(P) - G_s) = F_s 2^(G_start(P) - G_end(Q)), packed fp16 products
+        const half8 bb = ld8(&L.f16[16 * Q + l16][c]) * ld8(&L.xvh[p][c]);
+        akk = mfma32(ld8(&L.ka[16 * Pb + l16][c]), bb, akk);
+        aqk = mfma32(ld8(&L.qa[16 * Pb + l16][c]), bb, aqk);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * Pb + 4 * lq + e, ss = 16 * Q + l16;
+        const float lv = L.b[rr] * akk[e];
+        if (Pb == Q)
+          L.ldg[Pb][4 * lq + e][l16] = ss < rr ? lv : 0.f;
+        else
+          L.loff[rr][ss] = (_Float16)lv;
+        *reinterpret_cast<_Float16*>(blk + OFF_AQ + (2 * Pb + (ss >> 5)) * FRAG + frag_lane_byte(rr, ss)) =
+            (_Float16)(ss <= rr ? aqk[e] : 0.f);
+      }
+    }
+    if (w < PNB) {
+      {   // inverse of the diagonal block w by forward substitution. Column j = l / 4 runs on
+          // four lanes; lane q = l % 4 keeps x_s for s = q (mod 4) in xs[s / 4] and sums
+          // those terms (the block stores zeros on and above its diagonal, and xs starts at 0,
+          // so not-yet-computed terms add nothing); a butterfly gives all four lanes the sum.
+        const int Pb = w, j = l >> 2, q = l & 3;
+        // the lane's coefficients L[r][4k + q] (k <= (r - 1) / 4), loaded before the chain
+        float lv[16][4];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+          for (int k = 0; k <= (r - 1) / 4; ++k) lv[r][k] = L.ldg[Pb][r][4 * k + q];
+        float x[16], xs[4] = {0.f, 0.f, 0.f, 0.f};
+        x[0] = j == 0 ? 1.f : 0.f;
+        if (q == 0) xs[0] = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+          float part = 0.f;
+#pragma unroll
+          for (int k = 0; k <= (r - 1) / 4; ++k) part = __builtin_fmaf(lv[r][k], xs[k], part);
+          float tot = part + quad_xor1(part);
+          tot = tot + quad_xor2(tot);
+          x[r] = (r == j ? 1.f : 0.f) - tot;
+          if ((r & 3) == q) xs[r >> 2] = x[r];
+        }
+        if (q == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) L.u4.nd[16 * Pb + r][j] = x[r];
+        }
+      }
+    } else if (w >= PNB + 2) {
+      const int tt = t - (PNB + 2) * 64;   // 0 .. 127
+      // Kbar^T = (F * z)^T, z = decay from the end of block Q to the end of the chunk: the 8
+      // tokens s0 .. s0+7 of channel i are one lane's 16 bytes of fragment (i / 16, s0 / 32)
+      for (int it = tt; it < PD * (PC / 8); it += 128) {
+        const int i = it % PD, s0 = (it / PD) * 8, Q = s0 >> 4;
+        float zf = 1.f;
+        for (int R = Q + 1; R < PNB; ++R) zf *= L.bp[R][i];
+        const _Float16 z = (_Float16)zf;
+        half8 fk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fk[e] = L.f16[s0 + e][i];
+        *reinterpret_cast<half8*>(blk + OFF_KB + (2 * (i >> 4) + (s0 >> 5)) * FRAG + frag_lane_byte(i, s0)) =
+            fk * z;
+      }
+      // blocks (0,1) and (2,3) lie above the diagonal inside fragments (0,0) and (2,1) of T
+      // and A_qk: lanes 32..63, the second half of each fragment
+      {
+        const int which = tt >> 5, u = tt & 31;   // 4 half-fragments x 32 lanes x 16 bytes
+        const int base = (which & 1 ? OFF_AQ : OFF_T) + (which & 2 ? 5 : 0) * FRAG + FRAG / 2;
+        *reinterpret_cast<uint4*>(blk + base + 16 * u) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- waves 0-3: T column blocks -----------------------------------------------------------
+  switch (w) {
+    case 0: t_column<0>(L, blk, l16, lq); break;
+    case 1: t_column<1>(L, blk, l16, lq); break;
+    case 2: t_column<2>(L, blk, l16, lq); break;
+    case 3: t_column<3>(L, blk, l16, lq); break;
+    default: break;
+  }
+}
+
+// ---- state_pass_kernel: the sequential part ---------------------------------------------
+constexpr int SNW = 4;            // waves per work-group
+constexpr int SNT = 64 * SNW;
+constexpr int BLOCK_UNITS = 64 * FRAG / 16;   // 16-byte units of the fragments of a block
+
+struct StateLds {
+  char buf[2][BLOCK_USED];   // operand blocks of the current and the next chunk
 };
 
-template <int VS>
-__device__ __forceinline__ void load_stage(Stage<VS>& st, const PrefillLaunch& A, size_t tok0, int n,
-                                           int h, int H, int col0, int t, int w, int l16, int lq) {
-  constexpr int NCT = VS / 16;
+// Accumulator tiles lo (rows 0..15) and hi (rows 16..31) of a 32-row k block -> the fp16
+// B operand of v_mfma_f32_16x16x32_f16 (lane group g holds k rows 8g .. 8g+7). Lane group g of
+// an accumulator tile holds rows 4g .. 4g+3; the two swaps move rows across lane halves so
+// that every group ends with 8 consecutive rows.
+__device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
+  typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+  const half4 a = to_h4(lo), b = to_h4(hi);
+  const u2v au = __builtin_bit_cast(u2v, a), bu = __builtin_bit_cast(u2v, b);
+  // first value: lanes 0-31 keep rows 0..7 of lo, lanes 32-63 take rows 0..7 of hi;
+  // second value: rows 8..15 of lo (lanes 0-31) and of hi (lanes 32-63)
+  const auto s01 = __builtin_amdgcn_permlane32_swap(au[0], bu[0], false, false);
+  const auto s23 = __builtin_amdgcn_permlane32_swap(au[1], bu[1], false, false);
+  // per 16-lane row: the first value gets the lower four rows, the second the upper four
+  const auto t01 = __builtin_amdgcn_permlane16_swap(s01[0], s01[1], false, false);
+  const auto t23 = __builtin_amdgcn_permlane16_swap(s23[0], s23[1], false, false);
+  const u4v r = {t01[0], t23[0], t01[1], t23[1]};
+  return __builtin_bit_cast(half8, r);
+}
+
+// Loads of chunk c into the prefetch registers: the chunk's operand block (16-byte units
+// t + SNT j plus two bytes of 2^(G_C)) and the wave's V values (bf16 bits, one per register;
+// rows beyond the sequence read as 0).
+template <int NCW>
+__device__ __forceinline__ void state_prefetch(u4v (&pf)[BLOCK_UNITS / SNT], uint32_t& pfg,
+                                               uint32_t (&pv)[NCW][4][4], const char* blk0,
+                                               const PrefillLaunch& A, int c, int H, int lo, int len,
+                                               int h, int colw, int t, int l16, int lq) {
+  const char* bsrc = blk0 + (size_t)c * H * BLOCK_BYTES;
+#pragma unroll
+  for (int j = 0; j < BLOCK_UNITS / SNT; ++j) pf[j] = *reinterpret_cast<const u4v*>(bsrc + 16 * (t + SNT * j));
+  pfg = *reinterpret_cast<const uint16_t*>(bsrc + OFF_GAM + 2 * t);
   const size_t hstride = (size_t)H * PD;
-  const int m = t >> 5, c4 = (t & 31) * 4;
+  const int tok0 = lo + PC * c, n = min(PC, len - PC * c);
+  const __amdgpu_buffer_rsrc_t rv =
+      buffer_rsrc(A.t.v + (size_t)tok0 * hstride + (size_t)h * PD, (uint32_t)(n * hstride * 2));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * m + i;
-    uint2 kk = make_uint2(0, 0), qq = make_uint2(0, 0);
-    float4 av = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (r < n) {
-      const size_t off = (tok0 + r) * hstride + (size_t)h * PD + c4;
-      kk = *reinterpret_cast<const uint2*>(A.t.k + off);
-      qq = *reinterpret_cast<const uint2*>(A.t.q + off);
-      av = *reinterpret_cast<const float4*>(A.t.a + off);
-    }
-    st.k[i] = kk;
-    st.q[i] = qq;
-    st.a[i] = av;
-  }
+  for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-  for (int j = 0; j < Stage<VS>::NXT; ++j) {
-    const int it = w + PNW * j;
-    if (it < 4 * NCT) {
-      const int rt = it & 3, ct = it >> 2;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * lq + e;
-        st.v[j][e] = r < n ? A.t.v[(tok0 + r) * hstride + (size_t)h * PD + col0 + 16 * ct + l16] : 0u;
+        pv[ct][rt][e] = __builtin_amdgcn_raw_buffer_load_b16(
+            rv, (int)(((size_t)r * hstride + colw + 16 * ct + l16) * 2), 0, 0);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st.v[j][e] = 0u;
-    }
-  }
-  st.b = (t < n) ? A.t.b[(tok0 + t) * H + h] : 0.f;
 }
 
-template <int VS>
-__global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillLaunch A, int n_hg) {
-  constexpr int NVS = PD / VS, NCT = VS / 16;
-  constexpr int NS = 8 * NCT / PNW;                       // S tiles per wave
-  constexpr int NXT = Stage<VS>::NXT;
-  static_assert(8 * NCT % PNW == 0, "S tiles must divide among the waves");
-  __shared__ PfLds<VS> L;
+// One work-group per (sequence, head, slice of 64 * NCW value columns); wave w owns column
+// tiles w * NCW .. w * NCW + NCW - 1 of the slice. Work-groups run longest sequence first and
+// all slices of a head sit on one XCD (shared L2 for the operand blocks).
+template <int NCW>
+__global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaunch A,
+                                                         const int32_t* __restrict__ choff,
+                                                         const int32_t* __restrict__ ckoff,
+                                                         const int32_t* __restrict__ order,
+                                                         const char* __restrict__ blocks, int n_hg) {
+  constexpr int VSW = 64 * NCW;             // value columns per work-group
+  constexpr int NVS = PD / VSW;
+  constexpr int NPF = BLOCK_UNITS / SNT;    // 16-byte prefetch units per thread
+  __shared__ StateLds L;
   const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
   const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
   if (hg >= n_hg) return;
-  // Work-groups are dispatched in block order: sequence rank 0 (the longest; ties by index)
-  // first, so the longest recurrences start before the short ones fill the remaining CUs.
-  const int H = P.H, h = hg % H;
-  const int si = seq_by_rank(A.cu_seqlens, A.n_seq, hg / H);
+  const int H = P.H, h = hg % H, si = order[hg / H];
   const int t = threadIdx.x, w = t >> 6, l = t & 63, l16 = l & 15, lq = l >> 4;
 
-  const int lo = A.cu_seqlens[si], hi = A.cu_seqlens[si + 1], len = hi - lo;
-  int ck = 0;
-  if (A.ckpt_interval > 0)
-    for (int j = 0; j < si; ++j) ck += (A.cu_seqlens[j + 1] - A.cu_seqlens[j]) / A.ckpt_interval;
+  const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
+  const int nch = (len + PC - 1) / PC;
+  int ck = A.ckpt_interval > 0 ? ckoff[si] : 0;
   const int init = A.init_slot ? A.init_slot[si] : -1;
   const bool has_init = init >= 0 && init < P.num_slots;
   const size_t per = (size_t)H * PD * PD, hoff = (size_t)h * PD * PD;
-  const int col0 = vs * VS;
   const size_t hstride = (size_t)H * PD;
+  const int colw = vs * VSW + 16 * NCW * w;   // first column of the wave's tiles
+  const char* blk0 = blocks + ((size_t)choff[si] * H + h) * BLOCK_BYTES;
 
-  // State slice in accumulator layout. Wave w owns S tiles it = w + PNW*j: row tile
-  // it % 8 (key channels 16*rt + 4*lq + e), column tile it / 8 (col0 + 16*ct + l16).
-  f4 S[NS];
+  // S tiles (row tile rt, column tile ct) in accumulator layout: rows 16 rt + 4 lq + e,
+  // column colw + 16 ct + l16.
+  f4 S[NCW][8];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+  for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + 4 * lq + e;
-      S[j][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] : 0.f;
-    }
-  }
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * lq + e;
+        S[ct][rt][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] : 0.f;
+      }
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
 
-  // T and A_qk are lower triangular; their upper blocks stay zero for the whole kernel.
-  for (int i = t; i < PC * PC16; i += PNT) {
-    (&L.aqk[0][0])[i] = (_Float16)0.f;
-    (&L.t16[0][0])[i] = (_Float16)0.f;
-  }
+  // Prefetch registers: the operand block of a chunk (NPF units of 16 bytes per thread plus
+  // two bytes of 2^(G_C)) and the wave's V values (bf16 bits, one per register).
+  u4v pf[NPF];
+  uint32_t pfg;
+  uint32_t pv[NCW][4][4];
+  if (nch > 0) state_prefetch<NCW>(pf, pfg, pv, blk0, A, 0, H, lo, len, h, colw, t, l16, lq);
 
-  Stage<VS> st;
-  if (len > 0) load_stage<VS>(st, A, (size_t)lo, min(PC, len), h, H, col0, t, w, l16, lq);
-
-  for (int c0 = 0; c0 < len; c0 += PC) {
-    const int n = min(PC, len - c0);
-    const size_t tok0 = (size_t)(lo + c0);
-    lds_barrier();   // previous chunk's readers are done with every array below
-    // Lane indices re-derived through an opaque copy each chunk: LDS addresses are then
-    // recomputed per chunk instead of being hoisted out of the loop, where they would hold
-    // about a hundred VGPRs for the whole kernel.
-    int tid = (int)threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int t = tid, l = t & 63, l16 = l & 15, lq = l >> 4;
-
-    // ---- G = cumulative log2 a over the chunk's rows, per key channel: in registers over
-    //      the thread's 4 rows, then one exchange of the 16 row-group sums through LDS ------
-    const int m4 = t >> 5, c4 = (t & 31) * 4, Pm = m4 >> 2;
-    uint2 kcur[4], qcur[4];
-    f4 Gl[4];
-    {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c) {
+    const int n = min(PC, len - PC * c);
+    const int tok0 = lo + PC * c;
+    char* buf = L.buf[c & 1];
+    // The buffer written here was last read in chunk c - 2; every wave has passed the
+    // barrier of chunk c - 1 since.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += f4{flog2(st.a[i].x), flog2(st.a[i].y), flog2(st.a[i].z), flog2(st.a[i].w)};
-        Gl[i] = acc;
-        kcur[i] = st.k[i];
-        qcur[i] = st.q[i];
-      }
-      *reinterpret_cast<f4*>(&L.u4.part[m4][c4]) = acc;
-    }
-    if (t < PC) L.b[t] = st.b;
-    uint32_t vcur[NXT][4];
+    for (int j = 0; j < NPF; ++j) *reinterpret_cast<u4v*>(buf + 16 * (t + SNT * j)) = pf[j];
+    *reinterpret_cast<uint16_t*>(buf + OFF_GAM + 2 * t) = (uint16_t)pfg;
+    uint32_t vcur[NCW][4][4];
 #pragma unroll
-    for (int j = 0; j < NXT; ++j)
+    for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vcur[j][e] = st.v[j][e];
-    // prefetch the next chunk while this one computes
-    if (c0 + PC < len) load_stage<VS>(st, A, tok0 + PC, min(PC, len - c0 - PC), h, H, col0, t, w, l16, lq);
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vcur[ct][rt][e] = pv[ct][rt][e];
     lds_barrier();
+    // the last chunk re-reads its own block: no branch
+    state_prefetch<NCW>(pf, pfg, pv, blk0, A, min(c + 1, nch - 1), H, lo, len, h, colw, t, l16, lq);
 
-    // ---- decayed fp16 operands from registers: Ka/Qa (rows of block P times 2^(G - G_start(P))),
-    //      F (times 2^(G_end(P) - G)), Kt/Qt (times 2^G); every factor is <= 1. Each thread sums
-    //      the row-group totals in the same order, so G at a block's last row equals G_end. ------
-    {
-      // Row-group sums in increasing order: whole blocks before this one (a wave-uniform
-      // loop), then the four groups of this block. gs = G before the block, pre = G before
-      // the thread's rows, gend = G at the block's last row; every thread of a block adds the
-      // same terms in the same order, so G at a block's last row equals gend exactly.
-      f4 gs = {0.f, 0.f, 0.f, 0.f};
-      for (int mm = 0; mm < 4 * Pm; ++mm) gs += *reinterpret_cast<const f4*>(&L.u4.part[mm][c4]);
-      f4 blk[4];
+    const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
+    auto frag = [&](int off, int f) __attribute__((always_inline)) { return ld8(bh + (off + f * FRAG) / 2 + 8 * l); };
+
+    // S -> B operands (channel blocks kk = 0..3)
+    half8 sB[NCW][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) blk[q] = *reinterpret_cast<const f4*>(&L.u4.part[4 * Pm + q][c4]);
-      const int mq = m4 & 3;
-      const f4 s1 = gs + blk[0], s2 = s1 + blk[1], s3 = s2 + blk[2];
-      const f4 pre = mq == 0 ? gs : (mq == 1 ? s1 : (mq == 2 ? s2 : s3));
-      const f4 gend = s3 + blk[3];
-      if ((m4 & 3) == 3) {
-        *reinterpret_cast<f4*>(&L.ge[Pm][c4]) = gend;
-        if (Pm == PNB - 1)
-          *reinterpret_cast<f4*>(&L.gam[c4]) = f4{fexp2(gend[0]), fexp2(gend[1]), fexp2(gend[2]), fexp2(gend[3])};
-        const f4 dec = gs - gend;   // log2 of the inverse decay of this block, >= 0
-        if (dec[0] > DIAG_LOG2_LIMIT || dec[1] > DIAG_LOG2_LIMIT || dec[2] > DIAG_LOG2_LIMIT ||
-            dec[3] > DIAG_LOG2_LIMIT)
-          atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
+    for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sB[ct][kk] = acc_pair_to_b(S[ct][2 * kk], S[ct][2 * kk + 1]);
+
+    // X = V - Kt S
+    f4 X[NCW][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8 a = frag(OFF_KT, 4 * rt + kk);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = mfma32(a, sB[ct][kk], X[ct][rt]);
       }
-      const f4 y = {fexp2(gs[0]), fexp2(gs[1]), fexp2(gs[2]), fexp2(gs[3])};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * m4 + i;
-        const float kr[4] = {__uint_as_float(kcur[i].x << 16), __uint_as_float(kcur[i].x & 0xffff0000u),
-                             __uint_as_float(kcur[i].y << 16), __uint_as_float(kcur[i].y & 0xffff0000u)};
-        const float qr[4] = {__uint_as_float(qcur[i].x << 16), __uint_as_float(qcur[i].x & 0xffff0000u),
-                             __uint_as_float(qcur[i].y << 16), __uint_as_float(qcur[i].y & 0xffff0000u)};
-        f4 ka, qa, kt, qt, fv;
+      for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float G = pre[e] + Gl[i][e];
-          const float e1 = fexp2(G - gs[e]);
-          ka[e] = kr[e] * e1;
-          qa[e] = qr[e] * e1;
-          kt[e] = ka[e] * y[e];
-          qt[e] = qa[e] * y[e];
-          fv[e] = kr[e] * fexp2(gend[e] - G);
-        }
-        *reinterpret_cast<half4*>(&L.u1.a.ka[r][c4]) = to_h4(ka);
-        *reinterpret_cast<half4*>(&L.u1.a.qa[r][c4]) = to_h4(qa);
-        *reinterpret_cast<half4*>(&L.kt[r][c4]) = to_h4(kt);
-        *reinterpret_cast<half4*>(&L.qt[r][c4]) = to_h4(qt);
-        *reinterpret_cast<half4*>(&L.u3.f16[r][c4]) = to_h4(fv);
+        for (int e = 0; e < 4; ++e) X[ct][rt][e] = __uint_as_float(vcur[ct][rt][e] << 16) - X[ct][rt][e];
+    }
+    half8 xB[NCW][2];
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) xB[ct][kk] = acc_pair_to_b(X[ct][2 * kk], X[ct][2 * kk + 1]);
+
+    // W = T X (T is zero above the diagonal: token blocks kk <= rt / 2)
+    f4 W[NCW][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk <= rt / 2; ++kk) {
+        const half8 a = frag(OFF_T, 2 * rt + kk);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = mfma32(a, xB[ct][kk], W[ct][rt]);
       }
     }
-    lds_barrier();
+    half8 wB[NCW][2];
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) wB[ct][kk] = acc_pair_to_b(W[ct][2 * kk], W[ct][2 * kk + 1]);
 
-    // ---- A_kk, A_qk block pairs on matrix cores. Waves 0-3: diagonal pair (w, w), then the
-    //      inverse of that block by forward substitution (the wave's own LDS writes, no
-    //      barrier needed). Waves 4-7: the six off-diagonal pairs; waves 6-7 also Kbar^T. -----
+    // O = Qt S + A_qk W, stored as bf16; rows >= n fall outside the buffer range
     {
-      // pair index p = P(P+1)/2 + Q: diagonal pairs 0, 2, 5, 9; off-diagonal 1, 3, 4, 6, 7, 8
-      int pa, pb;
-      switch (w) {
-        case 0: pa = 0; pb = -1; break;
-        case 1: pa = 2; pb = -1; break;
-        case 2: pa = 5; pb = -1; break;
-        case 3: pa = 9; pb = -1; break;
-        case 4: pa = 1; pb = 7; break;
-        case 5: pa = 3; pb = 8; break;
-        case 6: pa = 4; pb = -1; break;
-        default: pa = 6; pb = -1; break;
-      }
-      for (int pi = 0; pi < 2; ++pi) {
-        const int p = pi == 0 ? pa : pb;
-        if (p < 0) break;
-        const int Pb = pair_p(p), Q = p - Pb * (Pb + 1) / 2;
-        {   // this pair's column factor, two channels per lane (read back by this wave only)
-          const int i0 = 2 * l;
-          const float g0 = Pb > 0 ? L.ge[Pb - 1][i0] : 0.f, g1 = Pb > 0 ? L.ge[Pb - 1][i0 + 1] : 0.f;
-          L.xvh[p][i0] = (_Float16)fexp2(g0 - L.ge[Q][i0]);
-          L.xvh[p][i0 + 1] = (_Float16)fexp2(g1 - L.ge[Q][i0 + 1]);
-        }
-        f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+      const __amdgpu_buffer_rsrc_t ro =
+          buffer_rsrc(A.t.o + (size_t)tok0 * hstride + (size_t)h * PD, (uint32_t)(n * hstride * 2));
 #pragma unroll
-        for (int kk = 0; kk < PD / 32; ++kk) {
-          const int c = 32 * kk + 8 * lq;
-          // k_s 2^(G_start(P) - G_s) = F_s 2^(G_start(P) - G_end(Q)), packed fp16 products
-          const half8 bb = ld8(&L.u3.f16[16 * Q + l16][c]) * ld8(&L.xvh[p][c]);
-          akk = mfma32(ld8(&L.u1.a.ka[16 * Pb + l16][c]), bb, akk);
-          aqk = mfma32(ld8(&L.u1.a.qa[16 * Pb + l16][c]), bb, aqk);
+      for (int rt = 0; rt < 4; ++rt) {
+        f4 O[NCW];
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) O[ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8 a = frag(OFF_QT, 4 * rt + kk);
+#pragma unroll
+          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(a, sB[ct][kk], O[ct]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 16 * Pb + 4 * lq + e, ss = 16 * Q + l16;
-          L.u2.l32[rr][ss] = ss < rr ? L.b[rr] * akk[e] : 0.f;
-          L.aqk[rr][ss] = (_Float16)(ss <= rr ? aqk[e] : 0.f);
+        for (int kk = 0; kk <= rt / 2; ++kk) {
+          const half8 a = frag(OFF_AQ, 2 * rt + kk);
+#pragma unroll
+          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(a, wB[ct][kk], O[ct]);
         }
-      }
-      if (w < PNB) {
-        {   // inverse of the diagonal block w by forward substitution. Column j = l / 4 runs on
-            // four lanes; lane q = l % 4 keeps x_s for s = q (mod 4) in xs[s / 4] and sums
-            // those terms (the block stores zeros on and above its diagonal, and xs starts at 0,
-            // so not-yet-computed terms add nothing); a butterfly gives all four lanes the sum.
-          const int Pb = w, j = l >> 2, q = l & 3;
-          float x[16], xs[4] = {0.f, 0.f, 0.f, 0.f};
-          x[0] = j == 0 ? 1.f : 0.f;
-          if (q == 0) xs[0] = x[0];
 #pragma unroll
-          for (int r = 1; r < 16; ++r) {
-            float part = 0.f;
+        for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-            for (int k = 0; k <= (r - 1) / 4; ++k)
-              part = __builtin_fmaf(L.u2.l32[16 * Pb + r][16 * Pb + 4 * k + q], xs[k], part);
-            float tot = part + __shfl_xor(part, 1);
-            tot = tot + __shfl_xor(tot, 2);
-            x[r] = (r == j ? 1.f : 0.f) - tot;
-            if ((r & 3) == q) xs[r >> 2] = x[r];
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * lq + e;
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f2bf(O[ct][e]), ro,
+                                                  (int)(((size_t)r * hstride + colw + 16 * ct + l16) * 2), 0, 0);
           }
-          if (q == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) L.u4.nd[16 * Pb + r][j] = x[r];
-          }
-        }
-      } else if (w >= PNB + 2) {   // Kbar^T = (F * zv)^T
-        for (int it = t - (PNB + 2) * 64; it < PD * (PC / 8); it += (PNW - PNB - 2) * 64) {
-          const int i = it % PD, s0 = (it / PD) * 8, Q = s0 >> 4;
-          const _Float16 z = (_Float16)fexp2(L.ge[PNB - 1][i] - L.ge[Q][i]);
-          half8 fk;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) fk[e] = L.u3.f16[s0 + e][i];
-          *reinterpret_cast<half8*>(&L.kbt[i][s0]) = fk * z;
-        }
       }
     }
-    lds_barrier();
 
-    // ---- waves 0-3: T column blocks; then every wave: fp16 copy of its S^T tiles --------
-    if (w < PNB) {
-      switch (w) {
-        case 0: t_column<0>(L, l16, lq); break;
-        case 1: t_column<1>(L, l16, lq); break;
-        case 2: t_column<2>(L, l16, lq); break;
-        default: t_column<3>(L, l16, lq); break;
+    // S <- Diag(2^(G_C)) S + Kbar^T W
+    const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      const f4 g = *reinterpret_cast<const f4*>(gam + 16 * rt + 4 * lq);
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) S[ct][rt] *= g;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const half8 a = frag(OFF_KB, 2 * rt + kk);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) S[ct][rt] = mfma32(a, wB[ct][kk], S[ct][rt]);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
-      *reinterpret_cast<half4*>(&L.u1.s16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(S[j]);
-    }
-    lds_barrier();
-
-    // ---- X = V - Kt S --------------------------------------------------------------------
-#pragma unroll
-    for (int j = 0; j < NXT; ++j) {
-      const int it = w + PNW * j;
-      if (it < 4 * NCT) {
-        const int rt = it & 3, ct = it >> 2;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < PD / 32; ++kk)
-          acc = mfma32(ld8(&L.kt[16 * rt + l16][32 * kk + 8 * lq]),
-                       ld8(&L.u1.s16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
-        f4 xv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xv[e] = __uint_as_float(vcur[j][e] << 16) - acc[e];
-        *reinterpret_cast<half4*>(&L.u2.x16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(xv);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_barrier();
-
-    // ---- W = T X (T is zero above the diagonal) --------------------------------------------
-#pragma unroll
-    for (int j = 0; j < NXT; ++j) {
-      const int it = w + PNW * j;
-      if (it < 4 * NCT) {
-        const int rt = it & 3, ct = it >> 2;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk <= (rt >> 1); ++kk)
-          acc = mfma32(ld8(&L.t16[16 * rt + l16][32 * kk + 8 * lq]),
-                       ld8(&L.u2.x16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
-        *reinterpret_cast<half4*>(&L.u3.w16t[16 * ct + l16][16 * rt + 4 * lq]) = to_h4(acc);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_barrier();
-
-    // ---- O = Qt S + A_qk W; S <- Diag(gamma) S + Kbar^T W -------------------------------------
-#pragma unroll
-    for (int j = 0; j < NXT; ++j) {
-      const int it = w + PNW * j;
-      if (it < 4 * NCT) {
-        const int rt = it & 3, ct = it >> 2;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < PD / 32; ++kk)
-          acc = mfma32(ld8(&L.qt[16 * rt + l16][32 * kk + 8 * lq]),
-                       ld8(&L.u1.s16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
-        for (int kk = 0; kk <= (rt >> 1); ++kk)
-          acc = mfma32(ld8(&L.aqk[16 * rt + l16][32 * kk + 8 * lq]),
-                       ld8(&L.u3.w16t[16 * ct + l16][32 * kk + 8 * lq]), acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rt + 4 * lq + e;
-          if (r < n) A.t.o[(tok0 + r) * hstride + (size_t)h * PD + col0 + 16 * ct + l16] = (uint16_t)f2bf(acc[e]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[j][e] *= L.gam[16 * rt + 4 * lq + e];
-#pragma unroll
-      for (int kk = 0; kk < PC / 32; ++kk)
-        S[j] = mfma32(ld8(&L.kbt[16 * rt + l16][32 * kk + 8 * lq]),
-                      ld8(&L.u3.w16t[16 * ct + l16][32 * kk + 8 * lq]), S[j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- checkpoint export inside the pass -------------------------------------------------
-    const int done = c0 + n;
+    const int done = PC * c + n;
     if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
       const int dst = A.ckpt_slot[ck++];
       if (dst >= 0 && dst < P.num_slots) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+        for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = 16 * rt + 4 * lq + e;
-            P.state[dst * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] = S[j][e];
-          }
-        }
+          for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = 16 * rt + 4 * lq + e;
+              P.state[dst * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] = S[ct][rt][e];
+            }
         if (t == 0 && h == 0 && vs == 0) {
           kda_slot_meta mm{pos0 + done, 0, 0, 0, 0};
           P.meta[dst] = mm;
@@ -554,14 +704,14 @@ __global__ __launch_bounds__(PNT) void prefill_chunk_kernel(PoolView P, PrefillL
   if (out >= 0 && out < P.num_slots) {
     __syncthreads();   // the init slot may be the out slot: every read of it is done
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int it = w + PNW * j, rt = it & 7, ct = it >> 3;
+    for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * rt + 4 * lq + e;
-        P.state[out * per + hoff + (size_t)row * PD + col0 + 16 * ct + l16] = S[j][e];
-      }
-    }
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + 4 * lq + e;
+          P.state[out * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] = S[ct][rt][e];
+        }
     if (t == 0 && h == 0 && vs == 0) {
       kda_slot_meta mm{pos0 + len, 0, 0, 0, 0};
       P.meta[out] = mm;
@@ -582,25 +732,49 @@ int device_cu_count() {
   return cus;
 }
 
-template <int VS>
-hipError_t launch_vs(const PoolView& p, const PrefillLaunch& a, int n_hg, hipStream_t s) {
-  const int blocks = ((n_hg + 7) / 8) * 8 * (PD / VS);
-  hipLaunchKernelGGL(prefill_chunk_kernel<VS>, dim3(blocks), dim3(PNT), 0, s, p, a, n_hg);
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
+
+template <int NCW>
+hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
+                        const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
+  const int n_hg = a.n_seq * p.H;
+  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (64 * NCW));
+  hipLaunchKernelGGL(state_pass_kernel<NCW>, dim3(nb), dim3(SNT), 0, s, p, a, choff, ckoff, order,
+                     blocks, n_hg);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks) {
+  if (dk != PD || chunk != PC || n_seq <= 0) return 0;
+  return plan_bytes(n_seq) + (size_t)n_chunks * H * BLOCK_BYTES;
+}
+
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
   if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
-  // One work-group per CU (LDS-bound). The per-chunk latency of a chain depends little on
-  // the slice width (the S-independent part dominates), so split value columns as long as
-  // the grid stays within two rounds of CUs; work-groups start longest sequence first.
-  const int n_hg = a.n_seq * p.H, cus = device_cu_count();
-  if (n_hg * 8 <= 2 * cus) return launch_vs<16>(p, a, n_hg, s);
-  if (n_hg * 4 <= 2 * cus) return launch_vs<32>(p, a, n_hg, s);
-  if (n_hg * 2 <= 2 * cus) return launch_vs<64>(p, a, n_hg, s);
-  return launch_vs<128>(p, a, n_hg, s);
+  if (a.n_seq <= 0) return hipSuccess;
+  char* ws = static_cast<char*>(a.workspace);
+  int32_t* choff = reinterpret_cast<int32_t*>(ws);
+  int32_t* ckoff = choff + (a.n_seq + 1);
+  int32_t* order = ckoff + a.n_seq;
+  char* blocks = ws + plan_bytes(a.n_seq);
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a.cu_seqlens, a.n_seq,
+                     a.ckpt_interval, choff, ckoff, order);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_chunks > 0) {
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(a.n_chunks * p.H)), dim3(PNT), 0, s, p, a,
+                       choff, blocks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // One work-group per CU (LDS-bound). Two slices of 64 columns per head while the grid fits in
+  // one round of CUs, else whole heads (each operand fragment then feeds two column tiles).
+  const int n_hg = a.n_seq * p.H;
+  if (n_hg * 2 <= device_cu_count()) return launch_state<1>(p, a, choff, ckoff, order, blocks, s);
+  return launch_state<2>(p, a, choff, ckoff, order, blocks, s);
 }
 
 }  // namespace kda

@@ -88,6 +88,7 @@ class KDAPool:
         check(lib.kda_ring_layout(byref(self.desc), off), "kda_ring_layout")
         self.ring_offsets = list(off)
         self.err_offset = lib.kda_meta_error_offset(byref(self.desc))
+        self._ws = None   # prefill workspace (torch allocation, grown on demand)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -120,12 +121,23 @@ class KDAPool:
                 _dev(v, torch.bfloat16, "v"), _dev(a, torch.float32, "a"),
                 _dev(b, torch.float32, "b"), _dev(o, torch.bfloat16, "o"))
 
+    def _workspace(self, n_tok: int, n_seq: int, chunk: int):
+        """Device workspace for a prefill of this size from torch's allocator, kept and grown
+        per pool (the library then allocates nothing). Returns (pointer, bytes)."""
+        need = lib.kda_prefill_workspace_bytes(self.handle, n_tok, n_seq, chunk)
+        if need == 0:
+            return None, 0
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws.data_ptr(), self._ws.numel()
+
     def _prefill_struct(self, n_tok, cu, init, out, ckpt, chunk, interval, ptrs):
         args = _abi.kda_prefill_args(*ptrs)
         args.n_seq = cu.np.size - 1
         args.n_tok = n_tok
         args.chunk = chunk
         args.ckpt_interval = interval
+        args.workspace, args.workspace_bytes = self._workspace(n_tok, args.n_seq, chunk)
         args.h_cu_seqlens, args.d_cu_seqlens = cu.h, cu.d
         if init is not None:
             args.h_init_slot, args.d_init_slot = init.h, init.d
