@@ -60,11 +60,14 @@ constexpr int FRAG = 1024;
 constexpr int OFF_KT = 0;             // Kt:     f = 4 rt + kk  (token tile rt, channel block kk)
 constexpr int OFF_QT = 16 * FRAG;     // Qt:     same
 constexpr int OFF_KB = 32 * FRAG;     // Kbar^T: f = 2 rt + kk  (channel tile rt < 8, token block kk)
-constexpr int OFF_T = 48 * FRAG;      // T:      f = 2 rt + kk  (token tile rt, token block kk <= rt/2)
-constexpr int OFF_AQ = 56 * FRAG;     // A_qk:   same
-constexpr int OFF_GAM = 64 * FRAG;    // 2^(G_C), fp32 [PD]
-constexpr int BLOCK_USED = 64 * FRAG + 4 * PD;
-constexpr int BLOCK_BYTES = 65 * FRAG;
+constexpr int OFF_T = 48 * FRAG;      // T:      f = tri_frag(rt, kk), token block kk <= rt / 2
+constexpr int OFF_AQ = 54 * FRAG;     // A_qk:   same
+constexpr int OFF_GAM = 60 * FRAG;    // 2^(G_C), fp32 [PD]
+constexpr int BLOCK_BYTES = 60 * FRAG + 4 * PD;   // 61952, a multiple of 256
+
+// Lower-triangular 64x64 operands keep only the fragments with kk <= rt / 2:
+// (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+__host__ __device__ constexpr int tri_frag(int rt, int kk) { return rt < 2 ? rt : 2 * rt - 2 + kk; }
 
 __device__ __forceinline__ int frag_lane_byte(int row, int k) {   // byte of A[row][k] in its fragment
   return ((row & 15) + 16 * ((k & 31) >> 3)) * 16 + (k & 7) * 2;
@@ -201,7 +204,7 @@ __device__ __forceinline__ void t_column(const PrepLds& L, char* blk, int l16, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * Pb + 4 * lq + e, col = 16 * Q + l16;
-      *reinterpret_cast<_Float16*>(blk + OFF_T + (2 * Pb + (col >> 5)) * FRAG + frag_lane_byte(row, col)) =
+      *reinterpret_cast<_Float16*>(blk + OFF_T + tri_frag(Pb, col >> 5) * FRAG + frag_lane_byte(row, col)) =
           (_Float16)(v[e] * bq);
     }
   };
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
           L.ldg[Pb][4 * lq + e][l16] = ss < rr ? lv : 0.f;
         else
           L.loff[rr][ss] = (_Float16)lv;
-        *reinterpret_cast<_Float16*>(blk + OFF_AQ + (2 * Pb + (ss >> 5)) * FRAG + frag_lane_byte(rr, ss)) =
+        *reinterpret_cast<_Float16*>(blk + OFF_AQ + tri_frag(Pb, ss >> 5) * FRAG + frag_lane_byte(rr, ss)) =
             (_Float16)(ss <= rr ? aqk[e] : 0.f);
       }
     }
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
       // and A_qk: lanes 32..63, the second half of each fragment
       {
         const int which = tt >> 5, u = tt & 31;   // 4 half-fragments x 32 lanes x 16 bytes
-        const int base = (which & 1 ? OFF_AQ : OFF_T) + (which & 2 ? 5 : 0) * FRAG + FRAG / 2;
+        const int base = (which & 1 ? OFF_AQ : OFF_T) + (which & 2 ? tri_frag(2, 1) : 0) * FRAG + FRAG / 2;
         *reinterpret_cast<uint4*>(blk + base + 16 * u) = make_uint4(0, 0, 0, 0);
       }
     }
@@ -456,18 +459,50 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
 // ---- state_pass_kernel: the sequential part ---------------------------------------------
 constexpr int SNW = 4;            // waves per work-group
 constexpr int SNT = 64 * SNW;
-constexpr int BLOCK_UNITS = 64 * FRAG / 16;   // 16-byte units of the fragments of a block
+constexpr int NPF = OFF_GAM / 16 / SNT;   // 16-byte fragment units per thread
+static_assert(NPF * SNT * 16 == OFF_GAM, "fragments split evenly over the threads");
 
-struct StateLds {
-  char buf[2][BLOCK_USED];   // operand blocks of the current and the next chunk
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+// LDS image of one chunk for a work-group with VSW value columns: the operand block, then
+// V[64][VSW] bf16 rows.
+template <int VSW>
+struct StateBuf {
+  static constexpr int BYTES = BLOCK_BYTES + PC * VSW * 2;
+  static constexpr int VROW_UNITS = VSW / 8;          // 16-byte units per V row
+  static constexpr int NV = PC * VROW_UNITS / SNT;    // V units per thread
 };
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i of
+// the wave writes lds_wave_base + 16 i. lds_wave_base must be wave-uniform. Issued as inline
+// assembly so that the compiler does not put a full vmcnt(0) wait in front of every later LDS
+// read; completion is awaited explicitly (lds_dma_wait) before the barrier that publishes the
+// buffer. M0 is saved and restored around the load; one wait state separates the M0 write
+// from the load that reads it.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_wave_base)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Accumulator tiles lo (rows 0..15) and hi (rows 16..31) of a 32-row k block -> the fp16
 // B operand of v_mfma_f32_16x16x32_f16 (lane group g holds k rows 8g .. 8g+7). Lane group g of
 // an accumulator tile holds rows 4g .. 4g+3; the two swaps move rows across lane halves so
-// that every group ends with 8 consecutive rows.
+// that every group ends with 8 consecutive rows. The same registers are the A operand of
+// the transposed product (A[l16][8 lq + i] with rows and columns exchanged).
 __device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
-  typedef uint32_t u2v __attribute__((ext_vector_type(2)));
   const half4 a = to_h4(lo), b = to_h4(hi);
   const u2v au = __builtin_bit_cast(u2v, a), bu = __builtin_bit_cast(u2v, b);
   // first value: lanes 0-31 keep rows 0..7 of lo, lanes 32-63 take rows 0..7 of hi;
@@ -481,32 +516,27 @@ __device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
   return __builtin_bit_cast(half8, r);
 }
 
-// Loads of chunk c into the prefetch registers: the chunk's operand block (16-byte units
-// t + SNT j plus two bytes of 2^(G_C)) and the wave's V values (bf16 bits, one per register;
-// rows beyond the sequence read as 0).
-template <int NCW>
-__device__ __forceinline__ void state_prefetch(u4v (&pf)[BLOCK_UNITS / SNT], uint32_t& pfg,
-                                               uint32_t (&pv)[NCW][4][4], const char* blk0,
-                                               const PrefillLaunch& A, int c, int H, int lo, int len,
-                                               int h, int colw, int t, int l16, int lq) {
+// Issue the LDS-direct loads of chunk c into buffer `buf`: the fragments of its operand block
+// (units t + SNT j), 2^(G_C) (wave 0, lanes 0-31), and the work-group's V columns. Rows past
+// the sequence re-read its last row: their T columns and Kbar rows are zero, so any finite
+// value there drops out, and O rows past the sequence are never stored.
+template <int VSW>
+__device__ __forceinline__ void state_fetch(const char* blk0, const PrefillLaunch& A, int c, int H,
+                                            int lo, int len, int h, int col0, int t, int w,
+                                            uint32_t buf) {
+  using SB = StateBuf<VSW>;
   const char* bsrc = blk0 + (size_t)c * H * BLOCK_BYTES;
+  const uint32_t wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(buf + 16 * 64 * w));
 #pragma unroll
-  for (int j = 0; j < BLOCK_UNITS / SNT; ++j) pf[j] = *reinterpret_cast<const u4v*>(bsrc + 16 * (t + SNT * j));
-  pfg = *reinterpret_cast<const uint16_t*>(bsrc + OFF_GAM + 2 * t);
-  const size_t hstride = (size_t)H * PD;
+  for (int j = 0; j < NPF; ++j) lds_dma16(bsrc + 16 * (t + SNT * j), wb + 16 * SNT * j);
+  if (t < 32) lds_dma16(bsrc + OFF_GAM + 16 * t, buf + OFF_GAM);
   const int tok0 = lo + PC * c, n = min(PC, len - PC * c);
-  const __amdgpu_buffer_rsrc_t rv =
-      buffer_rsrc(A.t.v + (size_t)tok0 * hstride + (size_t)h * PD, (uint32_t)(n * hstride * 2));
+  const uint16_t* vsrc = A.t.v + (size_t)h * PD + col0;
 #pragma unroll
-  for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * lq + e;
-        pv[ct][rt][e] = __builtin_amdgcn_raw_buffer_load_b16(
-            rv, (int)(((size_t)r * hstride + colw + 16 * ct + l16) * 2), 0, 0);
-      }
+  for (int j = 0; j < SB::NV; ++j) {
+    const int u = t + SNT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
+    lds_dma16(vsrc + (size_t)(tok0 + min(r, n - 1)) * H * PD + 8 * q, wb + BLOCK_BYTES + 16 * SNT * j);
+  }
 }
 
 // One work-group per (sequence, head, slice of 64 * NCW value columns); wave w owns column
@@ -520,13 +550,15 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
                                                          const char* __restrict__ blocks, int n_hg) {
   constexpr int VSW = 64 * NCW;             // value columns per work-group
   constexpr int NVS = PD / VSW;
-  constexpr int NPF = BLOCK_UNITS / SNT;    // 16-byte prefetch units per thread
-  __shared__ StateLds L;
+  using SB = StateBuf<VSW>;
+  __shared__ __attribute__((aligned(16))) char lds[2][SB::BYTES];
   const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
   const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
   if (hg >= n_hg) return;
   const int H = P.H, h = hg % H, si = order[hg / H];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, l16 = l & 15, lq = l >> 4;
+  // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, l16 = l & 15,
+            lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
   const int nch = (len + PC - 1) / PC;
@@ -534,9 +566,12 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
   const int init = A.init_slot ? A.init_slot[si] : -1;
   const bool has_init = init >= 0 && init < P.num_slots;
   const size_t per = (size_t)H * PD * PD, hoff = (size_t)h * PD * PD;
-  const size_t hstride = (size_t)H * PD;
-  const int colw = vs * VSW + 16 * NCW * w;   // first column of the wave's tiles
+  const int col0 = vs * VSW;                  // first column of the work-group
+  const int cw = 16 * NCW * w;                // first column of the wave, within the slice
+  const int colw = col0 + cw;
+  const int hst2 = H * PD * 2;
   const char* blk0 = blocks + ((size_t)choff[si] * H + h) * BLOCK_BYTES;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0][0], lds1 = (uint32_t)(uintptr_t)&lds[1][0];
 
   // S tiles (row tile rt, column tile ct) in accumulator layout: rows 16 rt + 4 lq + e,
   // column colw + 16 ct + l16.
@@ -552,35 +587,26 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
       }
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
 
-  // Prefetch registers: the operand block of a chunk (NPF units of 16 bytes per thread plus
-  // two bytes of 2^(G_C)) and the wave's V values (bf16 bits, one per register).
-  u4v pf[NPF];
-  uint32_t pfg;
-  uint32_t pv[NCW][4][4];
-  if (nch > 0) state_prefetch<NCW>(pf, pfg, pv, blk0, A, 0, H, lo, len, h, colw, t, l16, lq);
+  if (nch > 0) state_fetch<VSW>(blk0, A, 0, H, lo, len, h, col0, t, w, lds0);
 
   for (int c = 0; c < nch; ++c) {
     const int n = min(PC, len - PC * c);
     const int tok0 = lo + PC * c;
-    char* buf = L.buf[c & 1];
-    // The buffer written here was last read in chunk c - 2; every wave has passed the
-    // barrier of chunk c - 1 since.
-#pragma unroll
-    for (int j = 0; j < NPF; ++j) *reinterpret_cast<u4v*>(buf + 16 * (t + SNT * j)) = pf[j];
-    *reinterpret_cast<uint16_t*>(buf + OFF_GAM + 2 * t) = (uint16_t)pfg;
-    uint32_t vcur[NCW][4][4];
-#pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vcur[ct][rt][e] = pv[ct][rt][e];
+    // This wave's loads of chunk c are done once at most the stores issued after them (the
+    // 4 * NCW O stores of chunk c - 1, possibly followed by checkpoint stores) are pending;
+    // the barrier then publishes every wave's part of the buffer.
+    if (c == 0) vm_wait<0>(); else vm_wait<4 * NCW>();
     lds_barrier();
-    // the last chunk re-reads its own block: no branch
-    state_prefetch<NCW>(pf, pfg, pv, blk0, A, min(c + 1, nch - 1), H, lo, len, h, colw, t, l16, lq);
+    // Chunk c + 1 goes to the other buffer, last read in chunk c - 1: every wave has passed
+    // the barrier above since. The last chunk re-reads its own block: no branch.
+    state_fetch<VSW>(blk0, A, min(c + 1, nch - 1), H, lo, len, h, col0, t, w, (c & 1) ? lds0 : lds1);
 
+    const char* buf = lds[c & 1];
     const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
-    auto frag = [&](int off, int f) __attribute__((always_inline)) { return ld8(bh + (off + f * FRAG) / 2 + 8 * l); };
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + BLOCK_BYTES);
+    auto frag = [&](int off, int f) __attribute__((always_inline)) {
+      return ld8(bh + (off + f * FRAG) / 2 + 8 * l);
+    };
 
     // S -> B operands (channel blocks kk = 0..3)
     half8 sB[NCW][4];
@@ -593,18 +619,22 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
     f4 X[NCW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
+      half8 a[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) a[kk] = frag(OFF_KT, 4 * rt + kk);
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const half8 a = frag(OFF_KT, 4 * rt + kk);
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = mfma32(a, sB[ct][kk], X[ct][rt]);
-      }
+        for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = mfma32(a[kk], sB[ct][kk], X[ct][rt]);
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[ct][rt][e] = __uint_as_float(vcur[ct][rt][e] << 16) - X[ct][rt][e];
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t vbits = vb[(16 * rt + 4 * lq + e) * VSW + cw + 16 * ct + l16];
+          X[ct][rt][e] = __uint_as_float(vbits << 16) - X[ct][rt][e];
+        }
     }
     half8 xB[NCW][2];
 #pragma unroll
@@ -620,7 +650,7 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
       for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk <= rt / 2; ++kk) {
-        const half8 a = frag(OFF_T, 2 * rt + kk);
+        const half8 a = frag(OFF_T, tri_frag(rt, kk));
 #pragma unroll
         for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = mfma32(a, xB[ct][kk], W[ct][rt]);
       }
@@ -631,35 +661,35 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) wB[ct][kk] = acc_pair_to_b(W[ct][2 * kk], W[ct][2 * kk + 1]);
 
-    // O = Qt S + A_qk W, stored as bf16; rows >= n fall outside the buffer range
+    // O^T = S^T Qt^T + W^T A_qk^T: the operands of O = Qt S + A_qk W with their roles swapped.
+    // An accumulator tile then holds O[token 16 rt + l16][columns 4 lq .. 4 lq + 3 of tile
+    // ct], stored as 8 bf16 bytes; rows >= n fall outside the buffer range.
     {
       const __amdgpu_buffer_rsrc_t ro =
-          buffer_rsrc(A.t.o + (size_t)tok0 * hstride + (size_t)h * PD, (uint32_t)(n * hstride * 2));
+          buffer_rsrc(A.t.o + (size_t)tok0 * H * PD + (size_t)h * PD + colw, (uint32_t)(n * hst2));
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
+        half8 b[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b[kk] = frag(OFF_QT, 4 * rt + kk);
         f4 O[NCW];
 #pragma unroll
         for (int ct = 0; ct < NCW; ++ct) O[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const half8 a = frag(OFF_QT, 4 * rt + kk);
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(a, sB[ct][kk], O[ct]);
-        }
+          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(sB[ct][kk], b[kk], O[ct]);
 #pragma unroll
         for (int kk = 0; kk <= rt / 2; ++kk) {
-          const half8 a = frag(OFF_AQ, 2 * rt + kk);
+          const half8 bq = frag(OFF_AQ, tri_frag(rt, kk));
 #pragma unroll
-          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(a, wB[ct][kk], O[ct]);
+          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(wB[ct][kk], bq, O[ct]);
         }
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * lq + e;
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f2bf(O[ct][e]), ro,
-                                                  (int)(((size_t)r * hstride + colw + 16 * ct + l16) * 2), 0, 0);
-          }
+        for (int ct = 0; ct < NCW; ++ct) {
+          const u2v ob = __builtin_bit_cast(u2v, __builtin_convertvector(O[ct], bf4));
+          __builtin_amdgcn_raw_buffer_store_b64(ob, ro, (16 * rt + l16) * hst2 + 2 * (16 * ct + 4 * lq), 0, 0);
+        }
       }
     }
 
@@ -668,20 +698,22 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
       const f4 g = *reinterpret_cast<const f4*>(gam + 16 * rt + 4 * lq);
+      const half8 a0 = frag(OFF_KB, 2 * rt), a1 = frag(OFF_KB, 2 * rt + 1);
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) S[ct][rt] *= g;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const half8 a = frag(OFF_KB, 2 * rt + kk);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) S[ct][rt] = mfma32(a, wB[ct][kk], S[ct][rt]);
+      for (int ct = 0; ct < NCW; ++ct) {
+        S[ct][rt] *= g;
+        S[ct][rt] = mfma32(a0, wB[ct][0], S[ct][rt]);
+        S[ct][rt] = mfma32(a1, wB[ct][1], S[ct][rt]);
       }
     }
 
     // ---- checkpoint export inside the pass -------------------------------------------------
     const int done = PC * c + n;
     if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
-      const int dst = A.ckpt_slot[ck++];
+      // uniform index: a scalar load through the constant address space (no vector-memory
+      // wait behind the chunk's in-flight loads)
+      typedef const __attribute__((address_space(4))) int32_t* cptr;
+      const int dst = ((cptr)(uintptr_t)A.ckpt_slot)[ck++];
       if (dst >= 0 && dst < P.num_slots) {
 #pragma unroll
         for (int ct = 0; ct < NCW; ++ct)
@@ -699,6 +731,8 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
       }
     }
   }
+  // the last chunk's (redundant) loads into the idle buffer land before the work-group ends
+  vm_wait<0>();
 
   const int out = A.out_slot[si];
   if (out >= 0 && out < P.num_slots) {
@@ -771,9 +805,10 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     if (e != hipSuccess) return e;
   }
   // One work-group per CU (LDS-bound). Two slices of 64 columns per head while the grid fits in
-  // one round of CUs, else whole heads (each operand fragment then feeds two column tiles).
+  // two rounds of CUs (work-groups start longest sequence first, so the second round holds
+  // the short ones), else whole heads (each operand fragment then feeds two column tiles).
   const int n_hg = a.n_seq * p.H;
-  if (n_hg * 2 <= device_cu_count()) return launch_state<1>(p, a, choff, ckoff, order, blocks, s);
+  if (n_hg * 2 <= 2 * device_cu_count()) return launch_state<1>(p, a, choff, ckoff, order, blocks, s);
   return launch_state<2>(p, a, choff, ckoff, order, blocks, s);
 }
 
