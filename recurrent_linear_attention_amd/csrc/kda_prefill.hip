@@ -516,28 +516,55 @@ __device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
   return __builtin_bit_cast(half8, r);
 }
 
-// Issue the LDS-direct loads of chunk c into buffer `buf`: the fragments of its operand block
-// (units t + SNT j), 2^(G_C) (wave 0, lanes 0-31), and the work-group's V columns. Rows past
-// the sequence re-read its last row: their T columns and Kbar rows are zero, so any finite
-// value there drops out, and O rows past the sequence are never stored.
+// The LDS-direct loads of one chunk, in three groups, each issued as soon as the previous
+// chunk in the same buffer has no reader left for that part:
+//   kv()  : Kt and the work-group's V columns   (read by X)
+//   qta() : Qt, T and A_qk                      (read by W and O)
+//   kbg() : Kbar^T and 2^(G_C)                  (read by the state update)
+// Fragment units are t + SNT j of each part. Rows past the sequence re-read its last row of
+// V: their T columns and Kbar rows are zero, so any finite value there drops out, and O rows
+// past the sequence are never stored.
 template <int VSW>
-__device__ __forceinline__ void state_fetch(const char* blk0, const PrefillLaunch& A, int c, int H,
-                                            int lo, int len, int h, int col0, int t, int w,
-                                            uint32_t buf) {
+struct StateFetch {
   using SB = StateBuf<VSW>;
-  const char* bsrc = blk0 + (size_t)c * H * BLOCK_BYTES;
-  const uint32_t wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(buf + 16 * 64 * w));
+  static constexpr int PART = 16 * FRAG / 16 / SNT;          // units per thread of Kt, Qt, Kbar^T
+  static constexpr int TRI = 12 * FRAG / 16 / SNT;           // units per thread of T and A_qk
+  static_assert(PART * SNT * 16 == 16 * FRAG && TRI * SNT * 16 == 12 * FRAG, "even split");
+  static constexpr int N_KV = PART + SB::NV, N_QTA = PART + TRI;
+  const char* bsrc;          // operand block of the chunk
+  const uint16_t* vsrc;      // V[token 0 of the chunk][head][col0]
+  uint32_t buf, wb;          // LDS buffer, and its part for this wave
+  int n, hstr, t;
+  __device__ __forceinline__ StateFetch(const char* blk0, const PrefillLaunch& A, int c, int H, int lo,
+                                        int len, int h, int col0, int t_, int w, uint32_t buf_)
+      : bsrc(blk0 + (size_t)c * H * BLOCK_BYTES),
+        vsrc(A.t.v + (size_t)(lo + PC * c) * H * PD + (size_t)h * PD + col0),
+        buf(buf_),
+        wb((uint32_t)__builtin_amdgcn_readfirstlane((int)(buf_ + 16 * 64 * w))),
+        n(min(PC, len - PC * c)),
+        hstr(H * PD),
+        t(t_) {}
+  __device__ __forceinline__ void units(int off, int count) const {
 #pragma unroll
-  for (int j = 0; j < NPF; ++j) lds_dma16(bsrc + 16 * (t + SNT * j), wb + 16 * SNT * j);
-  if (t < 32) lds_dma16(bsrc + OFF_GAM + 16 * t, buf + OFF_GAM);
-  const int tok0 = lo + PC * c, n = min(PC, len - PC * c);
-  const uint16_t* vsrc = A.t.v + (size_t)h * PD + col0;
-#pragma unroll
-  for (int j = 0; j < SB::NV; ++j) {
-    const int u = t + SNT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
-    lds_dma16(vsrc + (size_t)(tok0 + min(r, n - 1)) * H * PD + 8 * q, wb + BLOCK_BYTES + 16 * SNT * j);
+    for (int j = 0; j < count; ++j) lds_dma16(bsrc + off + 16 * (t + SNT * j), wb + off + 16 * SNT * j);
   }
-}
+  __device__ __forceinline__ void kv() const {
+    units(OFF_KT, PART);
+#pragma unroll
+    for (int j = 0; j < SB::NV; ++j) {
+      const int u = t + SNT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
+      lds_dma16(vsrc + (size_t)min(r, n - 1) * hstr + 8 * q, wb + BLOCK_BYTES + 16 * SNT * j);
+    }
+  }
+  __device__ __forceinline__ void qta() const {
+    units(OFF_QT, PART);
+    units(OFF_T, TRI);
+  }
+  __device__ __forceinline__ void kbg() const {
+    units(OFF_KB, PART);
+    if (t < 32) lds_dma16(bsrc + OFF_GAM + 16 * t, buf + OFF_GAM);
+  }
+};
 
 // One work-group per (sequence, head, slice of 64 * NCW value columns); wave w owns column
 // tiles w * NCW .. w * NCW + NCW - 1 of the slice. Work-groups run longest sequence first and
@@ -587,19 +614,34 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
       }
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
 
-  if (nch > 0) state_fetch<VSW>(blk0, A, 0, H, lo, len, h, col0, t, w, lds0);
+  using SF = StateFetch<VSW>;
+  // Vector-memory operations a wave issues between the last load of chunk c (its kbg group,
+  // issued at the top of chunk c - 1) and the top of chunk c: the kv and qta groups of chunk
+  // c + 1 and the 4 * NCW O stores of chunk c - 1 (checkpoint stores only add to them). Waiting
+  // for at most that many to be pending completes chunk c's loads.
+  constexpr int PENDING = SF::N_KV + SF::N_QTA + 4 * NCW;
+  const int nlast = nch - 1;
+  auto sf = [&](int c) __attribute__((always_inline)) {
+    return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, w, (c & 1) ? lds1 : lds0);
+  };
+  if (nch > 0) {
+    const SF f0 = sf(0), f1 = sf(1);
+    f0.kbg();
+    f0.kv();
+    f0.qta();
+    f1.kv();
+    f1.qta();
+  }
 
   for (int c = 0; c < nch; ++c) {
     const int n = min(PC, len - PC * c);
     const int tok0 = lo + PC * c;
-    // This wave's loads of chunk c are done once at most the stores issued after them (the
-    // 4 * NCW O stores of chunk c - 1, possibly followed by checkpoint stores) are pending;
-    // the barrier then publishes every wave's part of the buffer.
-    if (c == 0) vm_wait<0>(); else vm_wait<4 * NCW>();
-    lds_barrier();
-    // Chunk c + 1 goes to the other buffer, last read in chunk c - 1: every wave has passed
-    // the barrier above since. The last chunk re-reads its own block: no branch.
-    state_fetch<VSW>(blk0, A, min(c + 1, nch - 1), H, lo, len, h, col0, t, w, (c & 1) ? lds0 : lds1);
+    if (c == 0) vm_wait<SF::N_KV + SF::N_QTA>(); else vm_wait<PENDING>();
+    lds_barrier();   // every wave's loads of chunk c have landed
+    // Kbar^T and 2^(G_C) of chunk c + 1 replace those of chunk c - 1, whose state update every
+    // wave finished before the barrier. Past the last chunk the loads repeat it: no branch.
+    sf(c + 1).kbg();
+    const SF next2 = sf(c + 2);   // its kv / qta groups replace this chunk's, once read
 
     const char* buf = lds[c & 1];
     const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
@@ -636,6 +678,8 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
           X[ct][rt][e] = __uint_as_float(vbits << 16) - X[ct][rt][e];
         }
     }
+    lds_barrier();   // every wave is done with Kt and V of this chunk
+    next2.kv();
     half8 xB[NCW][2];
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct)
@@ -692,6 +736,8 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
         }
       }
     }
+    lds_barrier();   // every wave is done with Qt, T and A_qk of this chunk
+    next2.qta();
 
     // S <- Diag(2^(G_C)) S + Kbar^T W
     const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
