@@ -183,9 +183,14 @@ kda_status kda_rollback(kda_pool* pool, int32_t B, const int32_t* h_slots,
  * index_copy.) One packed token buffer [prefill tokens | decode tokens | verify tokens]:
  * prefill sequences take the first prefill.n_tok rows (cu_seqlens relative to row 0),
  * n_decode decode tokens follow, then n_verify * n_pos verify tokens ([seq][pos] order).
- * o is written in the same packing. The three parts run on `stream` in that order with no
- * gather or scatter; the prefill's token pointers and the step slot arrays of `prefill`,
- * `decode` and `verify` are ignored in favour of the packed ones below.                  */
+ * o is written in the same packing, with no gather or scatter; the prefill's token pointers
+ * and the step slot arrays of `prefill`, `decode` and `verify` are ignored in favour of the
+ * packed ones below. Decode and verify touch only their own slots, so when the batch also
+ * has a prefill they run on a side stream owned by the pool (default priority, created on
+ * first use, destroyed by kda_pool_destroy) while the prefill's sequential pass runs on
+ * `stream`: forked by an event recorded on `stream` after the prefill's first kernels,
+ * joined by an event that `stream` waits on before the call returns. Everything enqueued on
+ * `stream` afterwards is ordered after all three parts.                                  */
 typedef struct {
   const void* q; const void* k; const void* v;   /* bf16 [n_total][H][d] */
   const float* a; const float* b;

@@ -50,7 +50,14 @@ hipError_t launch_rollback(const PoolView& p, int32_t B, const int32_t* d_slots,
 hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s);
 hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t s);
-hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
+// Called by launch_prefill once the S-independent part is enqueued and before the sequential
+// part: lets the caller start independent work that overlaps the latter.
+struct PrefillHook {
+  hipError_t (*fn)(void* ctx);
+  void* ctx;
+};
+hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s,
+                          const PrefillHook* after_prep = nullptr);
 // Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
 // shapes that run the token-by-token kernel).
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);

@@ -66,6 +66,10 @@ struct kda_pool {
   uint32_t epoch = 0;
   void* ws = nullptr;                  // prefill workspace used when the caller passes none
   size_t ws_bytes = 0;
+  // Side stream of mixed batches (default priority): decode and verify run there while the
+  // prefill's sequential pass runs on the caller's stream. Created on first use.
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
   // Mark-and-check: returns false if a slot repeats within one validation pass.
   void begin_pass() {
@@ -187,10 +191,11 @@ kda_status kda_pool_create(const kda_pool_desc* d, void* state, void* ring, void
 
 kda_status kda_pool_destroy(kda_pool* p) {
   if (!p) return fail(KDA_EINVAL, "null pool");
-  if (p->ws) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(p->ws);
-  }
+  if (p->ws || p->aux) (void)hipDeviceSynchronize();
+  if (p->ws) (void)hipFree(p->ws);
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+  if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+  if (p->aux) (void)hipStreamDestroy(p->aux);
   delete p;
   return KDA_OK;
 }
@@ -456,7 +461,44 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
                    static_cast<const uint16_t*>(m->v) + row * H * dv, m->a + row * H * dk,
                    m->b + row * H, static_cast<uint16_t*>(m->o) + row * H * dv);
   };
+  // Decode and verify touch only their own slots (checked distinct above), so they need no
+  // order against the prefill: with a prefill in the batch they go to the side stream once
+  // the prefill's S-independent kernel is enqueued, and the caller's stream waits for them
+  // before anything later.
+  struct StepLaunches {
+    kda_pool* p;
+    const kda_mixed_args* m;
+    kda::StepTensors dec, ver;
+    hipStream_t s;
+    bool fork;
+    hipError_t run(hipStream_t on) const {
+      hipError_t e = hipSuccess;
+      if (m->n_decode > 0) {
+        e = kda::launch_decode(p->view, dec, m->n_decode, m->d_decode_slots, on);
+        if (e != hipSuccess) return e;
+      }
+      if (m->n_verify > 0)
+        e = kda::launch_verify(p->view, ver, m->n_verify, m->n_pos, m->d_verify_slots, on);
+      return e;
+    }
+    static hipError_t forked(void* ctx) {
+      const StepLaunches* sl = static_cast<const StepLaunches*>(ctx);
+      hipError_t e = hipEventRecord(sl->p->ev_fork, sl->s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sl->p->aux, sl->p->ev_fork, 0);
+      if (e == hipSuccess) e = sl->run(sl->p->aux);
+      if (e == hipSuccess) e = hipEventRecord(sl->p->ev_join, sl->p->aux);
+      return e;
+    }
+  };
+  const bool steps = m->n_decode > 0 || m->n_verify > 0;
+  StepLaunches sl{p, m, part(n_pre), part(n_pre + m->n_decode), s, pre.n_seq > 0 && steps};
   hipError_t e = hipSuccess;
+  if (sl.fork && !p->aux) {
+    e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "mixed: side stream");
+  }
   if (pre.n_seq > 0) {
     void* ws = nullptr;
     st = prefill_workspace(p, &pre, n_chunks, &ws);
@@ -464,19 +506,18 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     kda::PrefillLaunch L{part(0), pre.n_seq, pre.n_tok, pre.chunk, pre.ckpt_interval,
                          pre.d_cu_seqlens, pre.d_init_slot, pre.d_out_slot, pre.d_ckpt_slot,
                          max_len, n_chunks, ws};
-    e = kda::launch_prefill(p->view, L, s);
+    const kda::PrefillHook hook{&StepLaunches::forked, &sl};
+    e = kda::launch_prefill(p->view, L, s, sl.fork ? &hook : nullptr);
     if (e != hipSuccess) return hip_fail(e, "mixed: prefill launch");
+    if (sl.fork) {
+      e = hipStreamWaitEvent(s, p->ev_join, 0);
+      if (e != hipSuccess) return hip_fail(e, "mixed: join");
+    }
+  } else if (steps) {
+    e = sl.run(s);
+    if (e != hipSuccess) return hip_fail(e, "mixed: decode / verify launch");
   }
-  if (m->n_decode > 0) {
-    e = kda::launch_decode(p->view, part(n_pre), m->n_decode, m->d_decode_slots, s);
-    if (e != hipSuccess) return hip_fail(e, "mixed: decode launch");
-  }
-  if (m->n_verify > 0) {
-    e = kda::launch_verify(p->view, part(n_pre + m->n_decode), m->n_verify, m->n_pos,
-                           m->d_verify_slots, s);
-    if (e != hipSuccess) return hip_fail(e, "mixed: verify launch");
-    for (int32_t i = 0; i < m->n_verify; ++i) p->slot_state[m->h_verify_slots[i]] = SLOT_PENDING;
-  }
+  for (int32_t i = 0; i < m->n_verify; ++i) p->slot_state[m->h_verify_slots[i]] = SLOT_PENDING;
   return KDA_OK;
 }
 

@@ -127,23 +127,20 @@ __global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_
     sc += (len + PC - 1) / PC;
     sk += ckpt_interval > 0 ? len / ckpt_interval : 0;
   }
+  // inclusive scan of the per-thread sums over the work-group (Hillis-Steele)
   part_c[t] = sc;
   part_k[t] = sk;
   __syncthreads();
-  if (t == 0) {   // exclusive scan of the per-thread sums (1024 entries, once per launch)
-    int ac = 0, ak = 0;
-    for (int i = 0; i < PLAN_THREADS; ++i) {
-      const int c = part_c[i], k = part_k[i];
-      part_c[i] = ac;
-      part_k[i] = ak;
-      ac += c;
-      ak += k;
-    }
-    choff[n_seq] = ac;
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+    const int vc = t >= off ? part_c[t - off] : 0, vk = t >= off ? part_k[t - off] : 0;
+    __syncthreads();
+    part_c[t] += vc;
+    part_k[t] += vk;
+    __syncthreads();
   }
-  __syncthreads();
-  sc = part_c[t];
-  sk = part_k[t];
+  if (t == PLAN_THREADS - 1) choff[n_seq] = part_c[t];
+  sc = part_c[t] - sc;   // exclusive
+  sk = part_k[t] - sk;
   for (int j = j0; j < j1; ++j) {
     const int len = cu[j + 1] - cu[j];
     choff[j] = sc;
@@ -832,8 +829,15 @@ size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_ch
   return plan_bytes(n_seq) + (size_t)n_chunks * H * BLOCK_BYTES;
 }
 
-hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
-  if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
+hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s,
+                          const PrefillHook* after_prep) {
+  if (p.dk != PD || a.chunk != PC) {
+    if (after_prep) {
+      const hipError_t e = after_prep->fn(after_prep->ctx);
+      if (e != hipSuccess) return e;
+    }
+    return launch_prefill_recurrent(p, a, s);
+  }
   if (a.n_seq <= 0) return hipSuccess;
   char* ws = static_cast<char*>(a.workspace);
   int32_t* choff = reinterpret_cast<int32_t*>(ws);
@@ -848,6 +852,10 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(a.n_chunks * p.H)), dim3(PNT), 0, s, p, a,
                        choff, blocks);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (after_prep) {
+    e = after_prep->fn(after_prep->ctx);
     if (e != hipSuccess) return e;
   }
   // One work-group per CU (LDS-bound). Two slices of 64 columns per head while the grid fits in
