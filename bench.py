@@ -7,9 +7,10 @@ kda_mixed_batch, then the ReplaySSM commit of the verified sequences -- on H=32 
 seeded (kda_inputs.mixed_workload) and resident in HBM before timing starts.
 
 Prints one JSON line. `value` = tokens per second of the whole step (16384 / step time).
-`roofline` describes the dominant kernel (the chunked prefill), timed with HIP events on the
-stream the library launches on, in a second timed pass that issues the same launches one by
-one. `cpu_baseline` times the CPU oracle on a bounded sample (a subset of heads).
+`roofline` describes the dominant part, the chunked prefill (one kda_prefill call: its plan,
+chunk_prep and state_pass kernels), timed with HIP events on the stream the library launches
+on, in a second timed pass that issues the same calls one by one. `cpu_baseline` times the CPU
+oracle on a bounded sample (a subset of heads).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -36,13 +37,17 @@ TOK_OUT_B = D * 2                           # o bf16
 RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
 
 
-# HBM traffic of one prefill launch of the mixed step, from rocprofv3 counter passes
-# (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) scaled by the counters' reading for a 1 GiB
-# device copy (FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them: factors 2.0 and
-# 1.0). Valid only for the kernel source it was measured on (first 16 hex digits of its
-# SHA-256); for any other source the bench reports traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "9f2fb1fffd275d77", "fetch_kib": 334688, "fetch_scale": 2.0,
-                   "write_kib": 142816, "write_scale": 1.0}
+# HBM traffic of one prefill call of the mixed step (its three kernels: plan, chunk_prep,
+# state_pass), from rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch)
+# scaled by the counters' reading for a 1 GiB device copy (FETCH_SIZE reads half the copied
+# bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid only for the kernel source it was
+# measured on (first 16 hex digits of its SHA-256); for any other source the bench reports
+# traffic as null.
+PREFILL_TRAFFIC = {"source_sha256_16": "648afdb72d37d5c9", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"prefill_plan_kernel": 4, "chunk_prep_kernel": 269310,
+                                 "state_pass_kernel<1>": 316120},
+                   "write_kib": {"prefill_plan_kernel": 0, "chunk_prep_kernel": 501650,
+                                 "state_pass_kernel<1>": 142817}}
 
 
 def prefill_traffic_bytes():
@@ -52,7 +57,8 @@ def prefill_traffic_bytes():
     t = PREFILL_TRAFFIC
     if sha != t["source_sha256_16"]:
         return None
-    return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
+    return int((sum(t["fetch_kib"].values()) * t["fetch_scale"]
+                + sum(t["write_kib"].values()) * t["write_scale"]) * 1024)
 
 
 def prefill_bytes(n_tok, H, n_out, n_init=0, n_ckpt=0):
@@ -219,7 +225,8 @@ def main():
     pre_gbs = byts["prefill"] / ms["prefill"] / 1e6
     roofline = {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": prefill_traffic_bytes(),
-                "kernel": "prefill (chunked, all sequences of the batch in one launch)",
+                "kernel": "prefill: one kda_prefill call over all sequences of the batch "
+                          "(plan, chunk_prep and state_pass kernels, back to back on one stream)",
                 "alg_bytes_per_launch": byts["prefill"]}
 
     cpu = None
