@@ -183,6 +183,28 @@ def test_prefill_validation_errors():
     assert lib.kda_prefill(p.h, byref(prefill_args(i32(0), i32())), None) == 0
 
 
+def test_prefill_workspace_size_and_checks():
+    p = HostPool(H=4, d=128)
+    s = [p.alloc()[1] for _ in range(3)]
+    p16 = HostPool(H=4, d=16)
+    # the token-by-token shape takes no workspace, nor does an empty call
+    assert lib.kda_prefill_workspace_bytes(p16.h, 1000, 3, 16) == 0
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 0, 64) == 0
+    # at most floor(1000 / 64) + 3 = 18 chunks, 61,952 bytes per (chunk, head), plus a small plan
+    need = lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64)
+    assert 18 * 4 * 61952 <= need < 19 * 4 * 61952
+    assert lib.kda_prefill_workspace_bytes(p.h, 1064, 3, 64) > need
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 4, 64) > need
+    # lengths 640 + 360 -> 10 + 6 chunks; a too-small or misaligned buffer fails validation
+    cu, out = i32(0, 640, 1000), i32(s[0], s[1])
+    a = prefill_args(cu, out, chunk=64)
+    a.workspace, a.workspace_bytes = FAKE, 16 * 4 * 61952 - 1
+    assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EWORKSPACE
+    assert b"workspace" in lib.kda_last_error()
+    a.workspace, a.workspace_bytes = FAKE + 16, need
+    assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EINVAL
+
+
 def test_mixed_batch_rejects_slot_overlap():
     p = HostPool()
     s = [p.alloc()[1] for _ in range(4)]

@@ -235,8 +235,9 @@ def test_prefill_ragged_with_resume_and_checkpoints(d):
 
 @pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 3), (32, 6), (32, 9)])
 def test_prefill_every_slice_width(H, n_seq):
-    """sequences x heads of 28, 96, 192 and 288 select value-slice widths 16, 32, 64 and 128
-    on a 256-CU part; each must match the oracle (sampled heads, ragged lengths)."""
+    """sequences x heads of 28, 96 and 192 run the state pass with two 64-column slices per
+    head, 288 with whole heads (on a 256-CU part); each must match the oracle (sampled heads,
+    ragged lengths, a resumed first sequence, checkpoints)."""
     rng = np.random.default_rng(60 + H + n_seq)
     lengths = [int(x) for x in rng.integers(1, 300, size=n_seq)]
     lengths[0] = 257
@@ -300,6 +301,93 @@ def test_prefill_is_deterministic():
         torch.cuda.synchronize()
         res.append((O.clone(), g.state.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+# ----------------------------------------------------------------------------- plan and workspace
+
+@pytest.mark.parametrize("n_seq,H", [(1500, 2), (9000, 1)])
+def test_prefill_many_short_sequences(n_seq, H):
+    """More sequences than the plan kernel has threads (several per thread in its scan), and
+    more than it orders by length (identity order); empty sequences and two-chunk ones among
+    them. Oracle per sequence from a zero state."""
+    from oracle import kda_scan
+    rng = np.random.default_rng(70 + n_seq)
+    lengths = rng.choice([0, 1, 2, 3, 65], size=n_seq, p=[0.2, 0.3, 0.2, 0.2, 0.1])
+    d = 128
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    g = kda.KDAPool(n_seq, H, d)
+    for _ in range(n_seq):
+        g.kda_slot_alloc()
+    O = g.kda_prefill(*tok_dev(tok), cu, list(range(n_seq)))
+    torch.cuda.synchronize()
+    t = tok.np
+    Oo = np.zeros((int(cu[-1]), H, d))
+    sample = set(rng.choice(n_seq, size=40, replace=False).tolist()) | {int(np.argmax(lengths))}
+    S_ref = {}
+    for i in range(n_seq):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        if hi == lo and i not in sample:
+            continue
+        S, Oi, _ = kda_scan(np.zeros((H, d, d)), t["q"][lo:hi], t["k"][lo:hi], t["v"][lo:hi],
+                            t["a"][lo:hi], t["b"][lo:hi])
+        Oo[lo:hi] = Oi
+        if i in sample:
+            S_ref[i] = S
+    assert rel_bf16(O, Oo) <= TOL
+    for i, S in S_ref.items():
+        assert rel(g.state[i], S) <= TOL, i
+    meta = g.meta_array()
+    np.testing.assert_array_equal(meta[:, 0], lengths)
+    assert g.kda_read_device_error() == 0
+
+
+def test_prefill_with_pool_owned_workspace():
+    """workspace = NULL through the C ABI: the pool allocates its own (and grows it for a
+    larger call); results are bit-identical to those with the caller's workspace."""
+    from ctypes import byref
+    from recurrent_linear_attention_amd import _abi
+    from recurrent_linear_attention_amd.pool import _ix, _stream
+    rng = np.random.default_rng(80)
+    H, d = 4, 128
+    g = kda.KDAPool(8, H, d)
+    for _ in range(8):
+        g.kda_slot_alloc()
+    for lengths in ([300, 0, 129, 64], [700, 1, 65, 190]):
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+        q, k, v, a, b = tok_dev(tok)
+        O1 = g.kda_prefill(q, k, v, a, b, cu, [0, 1, 2, 3])
+        S1 = g.state[:4].clone()
+        O2 = torch.empty_like(O1)
+        cu_ix, out_ix = _ix(cu, g.device), _ix([4, 5, 6, 7], g.device)
+        args = g._prefill_struct(int(cu[-1]), cu_ix, None, out_ix, None, 64, 0,
+                                 g._tok_ptrs(q, k, v, a, b, O2))
+        args.workspace, args.workspace_bytes = None, 0
+        assert _abi.lib.kda_prefill(g.handle, byref(args), _stream(None)) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(O1, O2)
+        assert torch.equal(S1, g.state[4:8])
+
+
+def test_mixed_batch_without_prefill():
+    """Only decode and verify parts: they run on the caller's stream, as separate calls would."""
+    H, d, P = 4, 128, 5
+    g, o = pools(8, H, d)
+    rng = np.random.default_rng(90)
+    ds, vs = [1, 4, 6], [0, 7]
+    put_states(g, o, ds + vs, ki.draw_states(rng, 5, H, d, d))
+    tok = ki.draw_tokens(rng, (len(ds) + len(vs) * P,), H, d, d)
+    O = g.kda_mixed_batch(*tok_dev(tok), [0], [], ds, vs, P)
+    torch.cuda.synchronize()
+    Od = o.decode(tok.slice(0, len(ds)).np, ds)
+    vt = {n: x[len(ds):].reshape((len(vs), P) + x.shape[1:]) for n, x in tok.np.items()}
+    Ov = o.verify(vt, vs)
+    assert rel_bf16(O[:len(ds)], Od) <= TOL
+    assert rel_bf16(O[len(ds):].reshape(len(vs), P, H, d), Ov) <= TOL
+    assert rel(g.state[ds], o.state[ds]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), ds + vs)
+    ring_check(g, o, vs)
 
 
 # ----------------------------------------------------------------------------- mixed batch
