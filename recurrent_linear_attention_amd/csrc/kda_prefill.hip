@@ -454,8 +454,8 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
 }
 
 // ---- state_pass_kernel: the sequential part ---------------------------------------------
-constexpr int SNW = 4;            // waves per work-group
-constexpr int SNT = 64 * SNW;
+constexpr int SNW = 4;            // compute waves per work-group (one per SIMD)
+constexpr int SNT = 64 * SNW;     // threads of one role: the compute waves, or the load waves
 constexpr int NPF = OFF_GAM / 16 / SNT;   // 16-byte fragment units per thread
 static_assert(NPF * SNT * 16 == OFF_GAM, "fragments split evenly over the threads");
 
@@ -566,8 +566,11 @@ struct StateFetch {
 // One work-group per (sequence, head, slice of 64 * NCW value columns); wave w owns column
 // tiles w * NCW .. w * NCW + NCW - 1 of the slice. Work-groups run longest sequence first and
 // all slices of a head sit on one XCD (shared L2 for the operand blocks).
-template <int NCW>
-__global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaunch A,
+// LOADERS: with 4, a second set of 4 waves issues every LDS-direct load and waits for it, so
+// the compute waves never stall on vector-memory issue (a CU accepts about one 1 KiB load per
+// ~27 cycles, ~70 KiB per chunk); with 0 the compute waves issue the loads themselves.
+template <int NCW, int LOADERS>
+__global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView P, PrefillLaunch A,
                                                          const int32_t* __restrict__ choff,
                                                          const int32_t* __restrict__ ckoff,
                                                          const int32_t* __restrict__ order,
@@ -580,8 +583,12 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
   const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
   if (hg >= n_hg) return;
   const int H = P.H, h = hg % H, si = order[hg / H];
-  // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar
-  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, l16 = l & 15,
+  // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar.
+  // Load waves (LOADERS > 0) are waves SNW .. SNW + 3; t and w index within a role.
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool loads = LOADERS == 0 || wave >= SNW;     // this wave issues the loads
+  const bool computes = LOADERS == 0 || wave < SNW;   // this wave runs the products
+  const int t = (int)threadIdx.x & (SNT - 1), w = wave & (SNW - 1), l = t & 63, l16 = l & 15,
             lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
@@ -607,21 +614,23 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * rt + 4 * lq + e;
-        S[ct][rt][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] : 0.f;
+        S[ct][rt][e] = has_init && computes
+                           ? P.state[init * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] : 0.f;
       }
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
 
   using SF = StateFetch<VSW>;
-  // Vector-memory operations a wave issues between the last load of chunk c (its kbg group,
-  // issued at the top of chunk c - 1) and the top of chunk c: the kv and qta groups of chunk
-  // c + 1 and the 4 * NCW O stores of chunk c - 1 (checkpoint stores only add to them). Waiting
-  // for at most that many to be pending completes chunk c's loads.
-  constexpr int PENDING = SF::N_KV + SF::N_QTA + 4 * NCW;
+  // Vector-memory operations a load-issuing wave issues between the last load of chunk c (its
+  // kbg group, issued at the top of chunk c - 1) and the top of chunk c: the kv and qta groups
+  // of chunk c + 1, and when the same waves compute, the 4 * NCW O stores of chunk c - 1
+  // (checkpoint stores only add to them). Waiting for at most that many to be pending
+  // completes chunk c's loads.
+  constexpr int PENDING = SF::N_KV + SF::N_QTA + (LOADERS ? 0 : 4 * NCW);
   const int nlast = nch - 1;
   auto sf = [&](int c) __attribute__((always_inline)) {
     return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, w, (c & 1) ? lds1 : lds0);
   };
-  if (nch > 0) {
+  if (nch > 0 && loads) {
     const SF f0 = sf(0), f1 = sf(1);
     f0.kbg();
     f0.kv();
@@ -633,11 +642,13 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
   for (int c = 0; c < nch; ++c) {
     const int n = min(PC, len - PC * c);
     const int tok0 = lo + PC * c;
-    if (c == 0) vm_wait<SF::N_KV + SF::N_QTA>(); else vm_wait<PENDING>();
+    if (loads) {
+      if (c == 0) vm_wait<SF::N_KV + SF::N_QTA>(); else vm_wait<PENDING>();
+    }
     lds_barrier();   // every wave's loads of chunk c have landed
     // Kbar^T and 2^(G_C) of chunk c + 1 replace those of chunk c - 1, whose state update every
     // wave finished before the barrier. Past the last chunk the loads repeat it: no branch.
-    sf(c + 1).kbg();
+    if (loads) sf(c + 1).kbg();
     const SF next2 = sf(c + 2);   // its kv / qta groups replace this chunk's, once read
 
     const char* buf = lds[c & 1];
@@ -647,15 +658,16 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
       return ld8(bh + (off + f * FRAG) / 2 + 8 * l);
     };
 
+    half8 sB[NCW][4], xB[NCW][2], wB[NCW][2];
+    f4 X[NCW][4], W[NCW][4];
+    if (computes) {
     // S -> B operands (channel blocks kk = 0..3)
-    half8 sB[NCW][4];
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) sB[ct][kk] = acc_pair_to_b(S[ct][2 * kk], S[ct][2 * kk + 1]);
 
     // X = V - Kt S
-    f4 X[NCW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       half8 a[4];
@@ -675,16 +687,16 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
           X[ct][rt][e] = __uint_as_float(vbits << 16) - X[ct][rt][e];
         }
     }
+    }
     lds_barrier();   // every wave is done with Kt and V of this chunk
-    next2.kv();
-    half8 xB[NCW][2];
+    if (loads) next2.kv();
+    if (computes) {
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) xB[ct][kk] = acc_pair_to_b(X[ct][2 * kk], X[ct][2 * kk + 1]);
 
     // W = T X (T is zero above the diagonal: token blocks kk <= rt / 2)
-    f4 W[NCW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
@@ -696,7 +708,6 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
         for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = mfma32(a, xB[ct][kk], W[ct][rt]);
       }
     }
-    half8 wB[NCW][2];
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
@@ -733,8 +744,10 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
         }
       }
     }
+    }
     lds_barrier();   // every wave is done with Qt, T and A_qk of this chunk
-    next2.qta();
+    if (loads) next2.qta();
+    if (!computes) continue;
 
     // S <- Diag(2^(G_C)) S + Kbar^T W
     const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
@@ -780,6 +793,7 @@ __global__ __launch_bounds__(SNT) void state_pass_kernel(PoolView P, PrefillLaun
   const int out = A.out_slot[si];
   if (out >= 0 && out < P.num_slots) {
     __syncthreads();   // the init slot may be the out slot: every read of it is done
+    if (!computes) return;
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
@@ -812,13 +826,13 @@ int device_cu_count() {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
 
-template <int NCW>
+template <int NCW, int LOADERS>
 hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
                         const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
   const int n_hg = a.n_seq * p.H;
   const int nb = ((n_hg + 7) / 8) * 8 * (PD / (64 * NCW));
-  hipLaunchKernelGGL(state_pass_kernel<NCW>, dim3(nb), dim3(SNT), 0, s, p, a, choff, ckoff, order,
-                     blocks, n_hg);
+  hipLaunchKernelGGL((state_pass_kernel<NCW, LOADERS>), dim3(nb), dim3(SNT + 64 * LOADERS), 0, s, p, a,
+                     choff, ckoff, order, blocks, n_hg);
   return hipGetLastError();
 }
 
@@ -862,8 +876,9 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
   // two rounds of CUs (work-groups start longest sequence first, so the second round holds
   // the short ones), else whole heads (each operand fragment then feeds two column tiles).
   const int n_hg = a.n_seq * p.H;
-  if (n_hg * 2 <= 2 * device_cu_count()) return launch_state<1>(p, a, choff, ckoff, order, blocks, s);
-  return launch_state<2>(p, a, choff, ckoff, order, blocks, s);
+  if (n_hg * 2 <= 2 * device_cu_count())
+    return launch_state<1, 4>(p, a, choff, ckoff, order, blocks, s);
+  return launch_state<2, 0>(p, a, choff, ckoff, order, blocks, s);
 }
 
 }  // namespace kda

@@ -342,6 +342,38 @@ def test_prefill_many_short_sequences(n_seq, H):
     assert g.kda_read_device_error() == 0
 
 
+def test_prefill_one_long_and_five_short():
+    """One long prompt (not first in the batch) and five short ones at 32 heads: the long one
+    starts first and the short ones share the remaining CUs. Checkpoints, a resumed short
+    sequence and the outputs must match the oracle."""
+    rng = np.random.default_rng(85)
+    H, d = 32, 128
+    lengths = [600, 3000, 600, 600, 600, 600]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    g, _ = pools(40, H, d)
+    st = ki.draw_states(rng, 1, H, d, d)
+    g.state[39] = st[0].to("cuda")
+    init = [-1, -1, 39, -1, -1, -1]
+    out = list(range(6))
+    interval = 512
+    n_ck = sum(L // interval for L in lengths)
+    cks = list(range(6, 6 + n_ck))
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks, ckpt_interval=interval)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    o = OPool(40, len(heads), d, d, 9)
+    for _ in range(40):
+        o.alloc()
+    o.state[39] = st[0][heads].double().numpy()
+    Oo = o.prefill(heads_np(tok, heads), cu, init, out, cks, interval)
+    assert rel_bf16(O[:, heads], Oo) <= TOL
+    for s_ in out + cks:
+        assert rel(g.state[s_][heads], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), out + cks)
+    assert g.kda_read_device_error() == 0
+
+
 def test_prefill_with_pool_owned_workspace():
     """workspace = NULL through the C ABI: the pool allocates its own (and grows it for a
     larger call); results are bit-identical to those with the caller's workspace."""
