@@ -454,21 +454,18 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
 }
 
 // ---- state_pass_kernel: the sequential part ---------------------------------------------
-constexpr int SNW = 4;            // compute waves per work-group (one per SIMD)
-constexpr int SNT = 64 * SNW;     // threads of one role: the compute waves, or the load waves
-constexpr int NPF = OFF_GAM / 16 / SNT;   // 16-byte fragment units per thread
-static_assert(NPF * SNT * 16 == OFF_GAM, "fragments split evenly over the threads");
 
 typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 // LDS image of one chunk for a work-group with VSW value columns: the operand block, then
 // V[64][VSW] bf16 rows.
-template <int VSW>
+template <int VSW, int NT>
 struct StateBuf {
   static constexpr int BYTES = BLOCK_BYTES + PC * VSW * 2;
   static constexpr int VROW_UNITS = VSW / 8;          // 16-byte units per V row
-  static constexpr int NV = PC * VROW_UNITS / SNT;    // V units per thread
+  static constexpr int NV = PC * VROW_UNITS / NT;     // V units per load-issuing thread
+  static_assert(NV * NT == PC * VROW_UNITS, "V rows split evenly over the threads");
 };
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i of
@@ -518,15 +515,15 @@ __device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
 //   kv()  : Kt and the work-group's V columns   (read by X)
 //   qta() : Qt, T and A_qk                      (read by W and O)
 //   kbg() : Kbar^T and 2^(G_C)                  (read by the state update)
-// Fragment units are t + SNT j of each part. Rows past the sequence re-read its last row of
+// Fragment units are t + NT j of each part (NT load-issuing threads). Rows past the sequence re-read its last row of
 // V: their T columns and Kbar rows are zero, so any finite value there drops out, and O rows
 // past the sequence are never stored.
-template <int VSW>
+template <int VSW, int NT>
 struct StateFetch {
-  using SB = StateBuf<VSW>;
-  static constexpr int PART = 16 * FRAG / 16 / SNT;          // units per thread of Kt, Qt, Kbar^T
-  static constexpr int TRI = 12 * FRAG / 16 / SNT;           // units per thread of T and A_qk
-  static_assert(PART * SNT * 16 == 16 * FRAG && TRI * SNT * 16 == 12 * FRAG, "even split");
+  using SB = StateBuf<VSW, NT>;
+  static constexpr int PART = 16 * FRAG / 16 / NT;           // units per thread of Kt, Qt, Kbar^T
+  static constexpr int TRI = 12 * FRAG / 16 / NT;            // units per thread of T and A_qk
+  static_assert(PART * NT * 16 == 16 * FRAG && TRI * NT * 16 == 12 * FRAG, "even split");
   static constexpr int N_KV = PART + SB::NV, N_QTA = PART + TRI;
   const char* bsrc;          // operand block of the chunk
   const uint16_t* vsrc;      // V[token 0 of the chunk][head][col0]
@@ -543,14 +540,14 @@ struct StateFetch {
         t(t_) {}
   __device__ __forceinline__ void units(int off, int count) const {
 #pragma unroll
-    for (int j = 0; j < count; ++j) lds_dma16(bsrc + off + 16 * (t + SNT * j), wb + off + 16 * SNT * j);
+    for (int j = 0; j < count; ++j) lds_dma16(bsrc + off + 16 * (t + NT * j), wb + off + 16 * NT * j);
   }
   __device__ __forceinline__ void kv() const {
     units(OFF_KT, PART);
 #pragma unroll
     for (int j = 0; j < SB::NV; ++j) {
-      const int u = t + SNT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
-      lds_dma16(vsrc + (size_t)min(r, n - 1) * hstr + 8 * q, wb + BLOCK_BYTES + 16 * SNT * j);
+      const int u = t + NT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
+      lds_dma16(vsrc + (size_t)min(r, n - 1) * hstr + 8 * q, wb + BLOCK_BYTES + 16 * NT * j);
     }
   }
   __device__ __forceinline__ void qta() const {
@@ -563,33 +560,53 @@ struct StateFetch {
   }
 };
 
-// One work-group per (sequence, head, slice of 64 * NCW value columns); wave w owns column
-// tiles w * NCW .. w * NCW + NCW - 1 of the slice. Work-groups run longest sequence first and
-// all slices of a head sit on one XCD (shared L2 for the operand blocks).
-// LOADERS: with 4, a second set of 4 waves issues every LDS-direct load and waits for it, so
-// the compute waves never stall on vector-memory issue (a CU accepts about one 1 KiB load per
-// ~27 cycles, ~70 KiB per chunk); with 0 the compute waves issue the loads themselves.
-template <int NCW, int LOADERS>
-__global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView P, PrefillLaunch A,
+// One work-group per (sequence, head, slice of VSW value columns); compute wave w owns columns
+// 16 w .. 16 w + 15 of the slice. Work-groups run longest sequence first and all slices of a
+// head sit on one XCD (shared L2 for the operand blocks).
+// CW compute waves (one per SIMD at most), each owning one 16-column tile of the state, and LW
+// load waves that issue every LDS-direct load and wait for it, so the compute waves never stall
+// on vector-memory issue (a CU accepts about one 1 KiB load per ~27 cycles; a chunk is 64-70 KiB).
+// A work-group covers VSW = 16 CW value columns: fewer compute waves per work-group mean less
+// LDS traffic per CU (every compute wave reads all 60 KiB of a chunk's fragments) and more
+// work-groups per head, each streaming the chunk's block (from L2 after the first).
+//
+// Load schedule, buffer c & 1 holding chunk c, one barrier before each group's first use:
+//   BX (before X):     Kt / V of chunk c have landed;          then Kbar^T / 2^(G_C) of c + 1 load
+//   BW (before W):     Qt / T / A_qk of chunk c have landed;  then Kt / V of chunk c + 2 load
+//   BS (before S'):    Kbar^T / 2^(G_C) of chunk c landed;     then Qt / T / A_qk of c + 2 load
+// Each group reloads into the buffer right after the barrier that follows its last reader, so
+// every group has about 1.6-1.75 chunks of lead. A load wave waits before each barrier until
+// only the operations issued after the awaited group are pending (the four groups that follow
+// it in issue order; the prologue issues kv(0), qta(0), kbg(0), kv(1), qta(1), which gives the
+// same counts from chunk 0 on). Lanes 0-31 of load wave 0 also load 2^(G_C) in each kbg group:
+// the counts leave that load out, so that wave waits for slightly more than it needs.
+template <int CW, int LW>
+__global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, PrefillLaunch A,
                                                          const int32_t* __restrict__ choff,
                                                          const int32_t* __restrict__ ckoff,
                                                          const int32_t* __restrict__ order,
                                                          const char* __restrict__ blocks, int n_hg) {
-  constexpr int VSW = 64 * NCW;             // value columns per work-group
+  constexpr int VSW = 16 * CW;              // value columns per work-group
   constexpr int NVS = PD / VSW;
-  using SB = StateBuf<VSW>;
+  constexpr int NTL = 64 * LW;              // load-issuing threads
+  using SB = StateBuf<VSW, NTL>;
+  using SF = StateFetch<VSW, NTL>;
+  constexpr int N_KBG = SF::PART;           // without the 2^(G_C) load
+  constexpr int WAIT_BX = SF::N_QTA + N_KBG + SF::N_KV + SF::N_QTA;
+  constexpr int WAIT_BW = N_KBG + SF::N_KV + SF::N_QTA + N_KBG;
+  constexpr int WAIT_BS = SF::N_KV + SF::N_QTA + N_KBG + SF::N_KV;
+  static_assert(WAIT_BX <= 63 && WAIT_BW <= 63 && WAIT_BS <= 63, "vmcnt holds at most 63");
   __shared__ __attribute__((aligned(16))) char lds[2][SB::BYTES];
   const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
   const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
   if (hg >= n_hg) return;
   const int H = P.H, h = hg % H, si = order[hg / H];
   // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar.
-  // Load waves (LOADERS > 0) are waves SNW .. SNW + 3; t and w index within a role.
+  // Load waves are waves CW .. CW + LW - 1; t and w index within a role.
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const bool loads = LOADERS == 0 || wave >= SNW;     // this wave issues the loads
-  const bool computes = LOADERS == 0 || wave < SNW;   // this wave runs the products
-  const int t = (int)threadIdx.x & (SNT - 1), w = wave & (SNW - 1), l = t & 63, l16 = l & 15,
-            lq = l >> 4;
+  const bool loads = wave >= CW;
+  const int w = loads ? wave - CW : wave, t = (int)threadIdx.x - 64 * (wave - w),
+            l = t & 63, l16 = l & 15, lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
   const int nch = (len + PC - 1) / PC;
@@ -598,59 +615,57 @@ __global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView
   const bool has_init = init >= 0 && init < P.num_slots;
   const size_t per = (size_t)H * PD * PD, hoff = (size_t)h * PD * PD;
   const int col0 = vs * VSW;                  // first column of the work-group
-  const int cw = 16 * NCW * w;                // first column of the wave, within the slice
+  const int cw = 16 * w;                      // first column of the wave, within the slice
   const int colw = col0 + cw;
   const int hst2 = H * PD * 2;
   const char* blk0 = blocks + ((size_t)choff[si] * H + h) * BLOCK_BYTES;
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0][0], lds1 = (uint32_t)(uintptr_t)&lds[1][0];
-
-  // S tiles (row tile rt, column tile ct) in accumulator layout: rows 16 rt + 4 lq + e,
-  // column colw + 16 ct + l16.
-  f4 S[NCW][8];
-#pragma unroll
-  for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * rt + 4 * lq + e;
-        S[ct][rt][e] = has_init && computes
-                           ? P.state[init * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] : 0.f;
-      }
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
-
-  using SF = StateFetch<VSW>;
-  // Vector-memory operations a load-issuing wave issues between the last load of chunk c (its
-  // kbg group, issued at the top of chunk c - 1) and the top of chunk c: the kv and qta groups
-  // of chunk c + 1, and when the same waves compute, the 4 * NCW O stores of chunk c - 1
-  // (checkpoint stores only add to them). Waiting for at most that many to be pending
-  // completes chunk c's loads.
-  constexpr int PENDING = SF::N_KV + SF::N_QTA + (LOADERS ? 0 : 4 * NCW);
   const int nlast = nch - 1;
-  auto sf = [&](int c) __attribute__((always_inline)) {
+  auto sf = [&](int c) __attribute__((always_inline)) {   // past the last chunk: repeat it
     return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, w, (c & 1) ? lds1 : lds0);
   };
-  if (nch > 0 && loads) {
-    const SF f0 = sf(0), f1 = sf(1);
-    f0.kbg();
-    f0.kv();
-    f0.qta();
-    f1.kv();
-    f1.qta();
+
+  if (loads) {
+    // ---- load waves ------------------------------------------------------------------------
+    if (nch > 0) {
+      const SF f0 = sf(0), f1 = sf(1);
+      f0.kv();
+      f0.qta();
+      f0.kbg();
+      f1.kv();
+      f1.qta();
+    }
+    for (int c = 0; c < nch; ++c) {
+      vm_wait<WAIT_BX>();
+      lds_barrier();   // BX
+      sf(c + 1).kbg();
+      vm_wait<WAIT_BW>();
+      lds_barrier();   // BW
+      sf(c + 2).kv();
+      vm_wait<WAIT_BS>();
+      lds_barrier();   // BS
+      sf(c + 2).qta();
+    }
+    vm_wait<0>();   // the last (repeated) loads land before the work-group ends
+    if (A.out_slot[si] >= 0 && A.out_slot[si] < P.num_slots) __syncthreads();
+    return;
   }
+
+  // ---- compute waves ---------------------------------------------------------------------------
+  // S tiles (row tile rt) in accumulator layout: rows 16 rt + 4 lq + e, column colw + l16.
+  f4 S[8];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + 4 * lq + e;
+      S[rt][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + colw + l16] : 0.f;
+    }
 
   for (int c = 0; c < nch; ++c) {
     const int n = min(PC, len - PC * c);
     const int tok0 = lo + PC * c;
-    if (loads) {
-      if (c == 0) vm_wait<SF::N_KV + SF::N_QTA>(); else vm_wait<PENDING>();
-    }
-    lds_barrier();   // every wave's loads of chunk c have landed
-    // Kbar^T and 2^(G_C) of chunk c + 1 replace those of chunk c - 1, whose state update every
-    // wave finished before the barrier. Past the last chunk the loads repeat it: no branch.
-    if (loads) sf(c + 1).kbg();
-    const SF next2 = sf(c + 2);   // its kv / qta groups replace this chunk's, once read
-
     const char* buf = lds[c & 1];
     const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
     const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + BLOCK_BYTES);
@@ -658,109 +673,106 @@ __global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView
       return ld8(bh + (off + f * FRAG) / 2 + 8 * l);
     };
 
-    half8 sB[NCW][4], xB[NCW][2], wB[NCW][2];
-    f4 X[NCW][4], W[NCW][4];
-    if (computes) {
-    // S -> B operands (channel blocks kk = 0..3)
+    // S -> B operands (channel blocks kk = 0..3); no LDS involved, ahead of the barrier
+    half8 sB[4], xB[2], wB[2];
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sB[ct][kk] = acc_pair_to_b(S[ct][2 * kk], S[ct][2 * kk + 1]);
+    for (int kk = 0; kk < 4; ++kk) sB[kk] = acc_pair_to_b(S[2 * kk], S[2 * kk + 1]);
+    lds_barrier();   // BX: Kt and V of this chunk have landed
 
+    // Each phase issues all its LDS reads, then (past a scheduling fence, so the compiler cannot
+    // interleave them back into short load / wait / MFMA runs) its independent MFMA chains: the
+    // waits count down over reads that are all in flight.
     // X = V - Kt S
+    f4 X[4], W[4];
+    {
+      half8 a[4][4];
+      uint32_t vv[4][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      half8 a[4];
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) a[kk] = frag(OFF_KT, 4 * rt + kk);
+        for (int kk = 0; kk < 4; ++kk) a[rt][kk] = frag(OFF_KT, 4 * rt + kk);
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[rt][e] = vb[(16 * rt + 4 * lq + e) * VSW + cw + l16];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) X[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) X[ct][rt] = mfma32(a[kk], sB[ct][kk], X[ct][rt]);
+        for (int rt = 0; rt < 4; ++rt) X[rt] = mfma32(a[rt][kk], sB[kk], X[rt]);
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t vbits = vb[(16 * rt + 4 * lq + e) * VSW + cw + 16 * ct + l16];
-          X[ct][rt][e] = __uint_as_float(vbits << 16) - X[ct][rt][e];
-        }
+        for (int e = 0; e < 4; ++e) X[rt][e] = __uint_as_float(vv[rt][e] << 16) - X[rt][e];
     }
-    }
-    lds_barrier();   // every wave is done with Kt and V of this chunk
-    if (loads) next2.kv();
-    if (computes) {
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) xB[ct][kk] = acc_pair_to_b(X[ct][2 * kk], X[ct][2 * kk + 1]);
+    for (int kk = 0; kk < 2; ++kk) xB[kk] = acc_pair_to_b(X[2 * kk], X[2 * kk + 1]);
+    lds_barrier();   // BW: Qt, T and A_qk of this chunk have landed; Kt and V are free
 
-    // W = T X (T is zero above the diagonal: token blocks kk <= rt / 2)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk <= rt / 2; ++kk) {
-        const half8 a = frag(OFF_T, tri_frag(rt, kk));
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) W[ct][rt] = mfma32(a, xB[ct][kk], W[ct][rt]);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) wB[ct][kk] = acc_pair_to_b(W[ct][2 * kk], W[ct][2 * kk + 1]);
-
+    // W = T X (T is zero above the diagonal: token blocks kk <= rt / 2), then
     // O^T = S^T Qt^T + W^T A_qk^T: the operands of O = Qt S + A_qk W with their roles swapped.
-    // An accumulator tile then holds O[token 16 rt + l16][columns 4 lq .. 4 lq + 3 of tile
-    // ct], stored as 8 bf16 bytes; rows >= n fall outside the buffer range.
+    // An accumulator tile then holds O[token 16 rt + l16][columns 4 lq .. 4 lq + 3 of the
+    // wave's tile], stored as 8 bf16 bytes; rows >= n fall outside the buffer range.
     {
+      half8 tf[6], b[4][4], q[6];
+#pragma unroll
+      for (int f = 0; f < 6; ++f) tf[f] = frag(OFF_T, f);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b[rt][kk] = frag(OFF_QT, 4 * rt + kk);
+#pragma unroll
+      for (int f = 0; f < 6; ++f) q[f] = frag(OFF_AQ, f);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        W[rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk <= rt / 2; ++kk) W[rt] = mfma32(tf[tri_frag(rt, kk)], xB[kk], W[rt]);
+      }
+      f4 O[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[rt] = mfma32(sB[kk], b[rt][kk], O[rt]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) wB[kk] = acc_pair_to_b(W[2 * kk], W[2 * kk + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kk = 0; kk <= rt / 2; ++kk) O[rt] = mfma32(wB[kk], q[tri_frag(rt, kk)], O[rt]);
       const __amdgpu_buffer_rsrc_t ro =
           buffer_rsrc(A.t.o + (size_t)tok0 * H * PD + (size_t)h * PD + colw, (uint32_t)(n * hst2));
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        half8 b[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b[kk] = frag(OFF_QT, 4 * rt + kk);
-        f4 O[NCW];
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) O[ct] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(sB[ct][kk], b[kk], O[ct]);
-#pragma unroll
-        for (int kk = 0; kk <= rt / 2; ++kk) {
-          const half8 bq = frag(OFF_AQ, tri_frag(rt, kk));
-#pragma unroll
-          for (int ct = 0; ct < NCW; ++ct) O[ct] = mfma32(wB[ct][kk], bq, O[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          const u2v ob = __builtin_bit_cast(u2v, __builtin_convertvector(O[ct], bf4));
-          __builtin_amdgcn_raw_buffer_store_b64(ob, ro, (16 * rt + l16) * hst2 + 2 * (16 * ct + 4 * lq), 0, 0);
-        }
+        const u2v ob = __builtin_bit_cast(u2v, __builtin_convertvector(O[rt], bf4));
+        __builtin_amdgcn_raw_buffer_store_b64(ob, ro, (16 * rt + l16) * hst2 + 8 * lq, 0, 0);
       }
     }
-    }
-    lds_barrier();   // every wave is done with Qt, T and A_qk of this chunk
-    if (loads) next2.qta();
-    if (!computes) continue;
+    lds_barrier();   // BS: Kbar^T and 2^(G_C) of this chunk have landed; Qt, T, A_qk are free
 
     // S <- Diag(2^(G_C)) S + Kbar^T W
-    const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
+    {
+      const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
+      half8 kb[8][2];
+      f4 g[8];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      const f4 g = *reinterpret_cast<const f4*>(gam + 16 * rt + 4 * lq);
-      const half8 a0 = frag(OFF_KB, 2 * rt), a1 = frag(OFF_KB, 2 * rt + 1);
+      for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        S[ct][rt] *= g;
-        S[ct][rt] = mfma32(a0, wB[ct][0], S[ct][rt]);
-        S[ct][rt] = mfma32(a1, wB[ct][1], S[ct][rt]);
-      }
+        for (int kk = 0; kk < 2; ++kk) kb[rt][kk] = frag(OFF_KB, 2 * rt + kk);
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) g[rt] = *reinterpret_cast<const f4*>(gam + 16 * rt + 4 * lq);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) S[rt] *= g[rt];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) S[rt] = mfma32(kb[rt][kk], wB[kk], S[rt]);
     }
 
     // ---- checkpoint export inside the pass -------------------------------------------------
@@ -772,14 +784,12 @@ __global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView
       const int dst = ((cptr)(uintptr_t)A.ckpt_slot)[ck++];
       if (dst >= 0 && dst < P.num_slots) {
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct)
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-          for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = 16 * rt + 4 * lq + e;
-              P.state[dst * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] = S[ct][rt][e];
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rt + 4 * lq + e;
+            P.state[dst * per + hoff + (size_t)row * PD + colw + l16] = S[rt][e];
+          }
         if (t == 0 && h == 0 && vs == 0) {
           kda_slot_meta mm{pos0 + done, 0, 0, 0, 0};
           P.meta[dst] = mm;
@@ -787,22 +797,17 @@ __global__ __launch_bounds__(SNT + 64 * LOADERS) void state_pass_kernel(PoolView
       }
     }
   }
-  // the last chunk's (redundant) loads into the idle buffer land before the work-group ends
-  vm_wait<0>();
 
   const int out = A.out_slot[si];
   if (out >= 0 && out < P.num_slots) {
     __syncthreads();   // the init slot may be the out slot: every read of it is done
-    if (!computes) return;
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * rt + 4 * lq + e;
-          P.state[out * per + hoff + (size_t)row * PD + colw + 16 * ct + l16] = S[ct][rt][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * lq + e;
+        P.state[out * per + hoff + (size_t)row * PD + colw + l16] = S[rt][e];
+      }
     if (t == 0 && h == 0 && vs == 0) {
       kda_slot_meta mm{pos0 + len, 0, 0, 0, 0};
       P.meta[out] = mm;
@@ -826,13 +831,13 @@ int device_cu_count() {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
 
-template <int NCW, int LOADERS>
+template <int CW, int LW>
 hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
                         const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
   const int n_hg = a.n_seq * p.H;
-  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (64 * NCW));
-  hipLaunchKernelGGL((state_pass_kernel<NCW, LOADERS>), dim3(nb), dim3(SNT + 64 * LOADERS), 0, s, p, a,
-                     choff, ckoff, order, blocks, n_hg);
+  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (16 * CW));
+  hipLaunchKernelGGL((state_pass_kernel<CW, LW>), dim3(nb), dim3(64 * (CW + LW)), 0, s, p, a, choff,
+                     ckoff, order, blocks, n_hg);
   return hipGetLastError();
 }
 
@@ -872,13 +877,13 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     e = after_prep->fn(after_prep->ctx);
     if (e != hipSuccess) return e;
   }
-  // One work-group per CU (LDS-bound). Two slices of 64 columns per head while the grid fits in
-  // two rounds of CUs (work-groups start longest sequence first, so the second round holds
-  // the short ones), else whole heads (each operand fragment then feeds two column tiles).
-  const int n_hg = a.n_seq * p.H;
-  if (n_hg * 2 <= 2 * device_cu_count())
-    return launch_state<1, 4>(p, a, choff, ckoff, order, blocks, s);
-  return launch_state<2, 0>(p, a, choff, ckoff, order, blocks, s);
+  // The narrowest slices whose grid fits in one round of CUs: a chain's latency per chunk falls
+  // with fewer compute waves per CU (less LDS traffic each), while more work-groups per head
+  // only pay off while CUs would otherwise idle. Larger batches take 64-column slices.
+  const int n_hg = a.n_seq * p.H, cus = device_cu_count();
+  if (n_hg * 8 <= cus) return launch_state<1, 2>(p, a, choff, ckoff, order, blocks, s);
+  if (n_hg * 4 <= cus) return launch_state<2, 2>(p, a, choff, ckoff, order, blocks, s);
+  return launch_state<4, 4>(p, a, choff, ckoff, order, blocks, s);
 }
 
 }  // namespace kda

@@ -233,11 +233,11 @@ def test_prefill_ragged_with_resume_and_checkpoints(d):
     meta_equal(g.meta_array(), o.meta(), out + cks)
 
 
-@pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 3), (32, 6), (32, 9)])
+@pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 2), (32, 3), (32, 9)])
 def test_prefill_every_slice_width(H, n_seq):
-    """sequences x heads of 28, 96 and 192 run the state pass with two 64-column slices per
-    head, 288 with whole heads (on a 256-CU part); each must match the oracle (sampled heads,
-    ragged lengths, a resumed first sequence, checkpoints)."""
+    """sequences x heads of 28, 64 and 96 / 288 run the state pass with 16-, 32- and 64-column
+    slices (on a 256-CU part); each must match the oracle (sampled heads, ragged lengths, a
+    resumed first sequence, checkpoints)."""
     rng = np.random.default_rng(60 + H + n_seq)
     lengths = [int(x) for x in rng.integers(1, 300, size=n_seq)]
     lengths[0] = 257
