@@ -26,6 +26,9 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the state pass works on its accumulators with VALU
+    # instructions (decay, conversions) every chunk, which AGPRs would turn into register moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

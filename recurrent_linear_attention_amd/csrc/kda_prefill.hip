@@ -20,7 +20,7 @@
 // sequence is a few hundred MFMA cycles instead of the whole chunk computation.
 //   * chunk_prep_kernel writes each chunk's operands as fp16 16x32 A-operand fragments of
 //     v_mfma_f32_16x16x32_f16 in lane order (one 1 KiB fragment = 64 lanes x 16 bytes), so the
-//     state pass copies a chunk's 64.5 KiB block into LDS with coalesced 16-byte loads and
+//     state pass copies a chunk's 60.5 KiB block into LDS with coalesced 16-byte loads and
 //     reads every fragment with one conflict-free ds_read_b128 per lane.
 //   * state_pass_kernel keeps the state S in fp32 MFMA accumulators for the whole sequence.
 //     The accumulator tiles of S, X and W become B operands of the next product in registers:
@@ -52,12 +52,13 @@ constexpr int NPAIR = PNB * (PNB + 1) / 2;
 constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
 constexpr int PC16 = PC + 8;      // row pitch (halves) of [.][PC] fp16 arrays
 constexpr float DIAG_DECAY_MIN = 1.f / 16384.f;   // 2^-14
+constexpr int LDS_PER_CU = 160 * 1024;   // gfx950: LDS of one CU, the most one work-group may hold
 
 // ---- per-(chunk, head) operand block --------------------------------------------------------
 // A fragment holds a 16 x 32 fp16 tile A[16][32] as the A operand of v_mfma_f32_16x16x32_f16:
 // lane L = l16 + 16 * lq owns A[l16][8 lq .. 8 lq + 7] at bytes 16 L .. 16 L + 15.
 constexpr int FRAG = 1024;
-constexpr int OFF_KT = 0;             // Kt:     f = 4 rt + kk  (token tile rt, channel block kk)
+constexpr int OFF_KT = 0;             // -Kt:    f = 4 rt + kk  (token tile rt, channel block kk)
 constexpr int OFF_QT = 16 * FRAG;     // Qt:     same
 constexpr int OFF_KB = 32 * FRAG;     // Kbar^T: f = 2 rt + kk  (channel tile rt < 8, token block kk)
 constexpr int OFF_T = 48 * FRAG;      // T:      f = tri_frag(rt, kk), token block kk <= rt / 2
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
       for (int e = 0; e < 4; ++e) {
         ka[e] = kr[e] * e1[e];
         qa[e] = qr[e] * e1[e];
-        kt[e] = ka[e] * gsp[e];
+        kt[e] = -(ka[e] * gsp[e]);   // stored negated: X = V + (-Kt) S
         qt[e] = qa[e] * gsp[e];
         fv[e] = kr[e] * e2[e];
       }
@@ -459,19 +460,21 @@ typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 // LDS image of one chunk for a work-group with VSW value columns: the operand block, then
-// V[64][VSW] bf16 rows.
+// V[64][VSW] bf16 rows. With more load-issuing threads than V units, the threads past the
+// last unit repeat the loads of the first ones (same bytes to the same place).
 template <int VSW, int NT>
 struct StateBuf {
   static constexpr int BYTES = BLOCK_BYTES + PC * VSW * 2;
   static constexpr int VROW_UNITS = VSW / 8;          // 16-byte units per V row
-  static constexpr int NV = PC * VROW_UNITS / NT;     // V units per load-issuing thread
-  static_assert(NV * NT == PC * VROW_UNITS, "V rows split evenly over the threads");
+  static constexpr int VUNITS = PC * VROW_UNITS;
+  static constexpr int NV = (VUNITS + NT - 1) / NT;   // V units per load-issuing thread
+  static_assert((NV * NT) % VUNITS == 0, "V rows split evenly over the threads");
 };
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i of
 // the wave writes lds_wave_base + 16 i. lds_wave_base must be wave-uniform. Issued as inline
 // assembly so that the compiler does not put a full vmcnt(0) wait in front of every later LDS
-// read; completion is awaited explicitly (lds_dma_wait) before the barrier that publishes the
+// read; completion is awaited explicitly (vm_wait) before the barrier that publishes the
 // buffer. M0 is saved and restored around the load; one wait state separates the M0 write
 // from the load that reads it.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_wave_base) {
@@ -512,12 +515,12 @@ __device__ __forceinline__ half8 acc_pair_to_b(f4 lo, f4 hi) {
 
 // The LDS-direct loads of one chunk, in three groups, each issued as soon as the previous
 // chunk in the same buffer has no reader left for that part:
-//   kv()  : Kt and the work-group's V columns   (read by X)
-//   qta() : Qt, T and A_qk                      (read by W and O)
-//   kbg() : Kbar^T and 2^(G_C)                  (read by the state update)
-// Fragment units are t + NT j of each part (NT load-issuing threads). Rows past the sequence re-read its last row of
-// V: their T columns and Kbar rows are zero, so any finite value there drops out, and O rows
-// past the sequence are never stored.
+//   kv()  : -Kt and the work-group's V columns   (read by X)
+//   qta() : Qt, T and A_qk                       (read by W and O)
+//   kbg() : Kbar^T and 2^(G_C)                   (read by the state update)
+// Fragment units are t + NT j of each part (NT load-issuing threads). Rows past the sequence
+// re-read its last row of V: their T columns and Kbar rows are zero, so any finite value there
+// drops out, and O rows past the sequence are never stored.
 template <int VSW, int NT>
 struct StateFetch {
   using SB = StateBuf<VSW, NT>;
@@ -546,8 +549,11 @@ struct StateFetch {
     units(OFF_KT, PART);
 #pragma unroll
     for (int j = 0; j < SB::NV; ++j) {
-      const int u = t + NT * j, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
-      lds_dma16(vsrc + (size_t)min(r, n - 1) * hstr + 8 * q, wb + BLOCK_BYTES + 16 * NT * j);
+      const int u = (t + NT * j) % SB::VUNITS, r = u / SB::VROW_UNITS, q = u % SB::VROW_UNITS;
+      // the destination is uniform per wave: unit u lands at 16 u, and the wave's units are
+      // consecutive (NT and VUNITS are multiples of 64)
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(buf + BLOCK_BYTES + 16 * (u - (t & 63))));
+      lds_dma16(vsrc + (size_t)min(r, n - 1) * hstr + 8 * q, dst);
     }
   }
   __device__ __forceinline__ void qta() const {
@@ -560,19 +566,17 @@ struct StateFetch {
   }
 };
 
-// One work-group per (sequence, head, slice of VSW value columns); compute wave w owns columns
-// 16 w .. 16 w + 15 of the slice. Work-groups run longest sequence first and all slices of a
-// head sit on one XCD (shared L2 for the operand blocks).
-// CW compute waves (one per SIMD at most), each owning one 16-column tile of the state, and LW
+// One work-group per (sequence, head, slice of VSW value columns). Work-groups run longest
+// sequence first and all slices of a head sit on one XCD (shared L2 for the operand blocks).
+// CW compute waves, each owning TPW 16-column tiles of the state (VSW = 16 CW TPW), and LW
 // load waves that issue every LDS-direct load and wait for it, so the compute waves never stall
-// on vector-memory issue (a CU accepts about one 1 KiB load per ~27 cycles; a chunk is 64-70 KiB).
-// A work-group covers VSW = 16 CW value columns: fewer compute waves per work-group mean less
-// LDS traffic per CU (every compute wave reads all 60 KiB of a chunk's fragments) and more
-// work-groups per head, each streaming the chunk's block (from L2 after the first).
+// on vector-memory issue. Per chunk every compute wave reads all 60 KiB of the chunk's
+// fragments from LDS (a wave drains about 35 bytes per cycle, a CU 128), and each fragment
+// feeds TPW products.
 //
 // Load schedule, buffer c & 1 holding chunk c, one barrier before each group's first use:
-//   BX (before X):     Kt / V of chunk c have landed;          then Kbar^T / 2^(G_C) of c + 1 load
-//   BW (before W):     Qt / T / A_qk of chunk c have landed;  then Kt / V of chunk c + 2 load
+//   BX (before X):     -Kt / V of chunk c have landed;         then Kbar^T / 2^(G_C) of c + 1 load
+//   BW (before W):     Qt / T / A_qk of chunk c have landed;  then -Kt / V of chunk c + 2 load
 //   BS (before S'):    Kbar^T / 2^(G_C) of chunk c landed;     then Qt / T / A_qk of c + 2 load
 // Each group reloads into the buffer right after the barrier that follows its last reader, so
 // every group has about 1.6-1.75 chunks of lead. A load wave waits before each barrier until
@@ -580,13 +584,13 @@ struct StateFetch {
 // it in issue order; the prologue issues kv(0), qta(0), kbg(0), kv(1), qta(1), which gives the
 // same counts from chunk 0 on). Lanes 0-31 of load wave 0 also load 2^(G_C) in each kbg group:
 // the counts leave that load out, so that wave waits for slightly more than it needs.
-template <int CW, int LW>
+template <int CW, int TPW, int LW>
 __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, PrefillLaunch A,
                                                          const int32_t* __restrict__ choff,
                                                          const int32_t* __restrict__ ckoff,
                                                          const int32_t* __restrict__ order,
                                                          const char* __restrict__ blocks, int n_hg) {
-  constexpr int VSW = 16 * CW;              // value columns per work-group
+  constexpr int VSW = 16 * CW * TPW;        // value columns per work-group
   constexpr int NVS = PD / VSW;
   constexpr int NTL = 64 * LW;              // load-issuing threads
   using SB = StateBuf<VSW, NTL>;
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   const bool has_init = init >= 0 && init < P.num_slots;
   const size_t per = (size_t)H * PD * PD, hoff = (size_t)h * PD * PD;
   const int col0 = vs * VSW;                  // first column of the work-group
-  const int cw = 16 * w;                      // first column of the wave, within the slice
+  const int cw = 16 * TPW * w;                // first column of the wave, within the slice
   const int colw = col0 + cw;
   const int hst2 = H * PD * 2;
   const char* blk0 = blocks + ((size_t)choff[si] * H + h) * BLOCK_BYTES;
@@ -625,7 +629,6 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   auto sf = [&](int c) __attribute__((always_inline)) {   // past the last chunk: repeat it
     return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, w, (c & 1) ? lds1 : lds0);
   };
-
   if (loads) {
     // ---- load waves ------------------------------------------------------------------------
     if (nch > 0) {
@@ -653,15 +656,36 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   }
 
   // ---- compute waves ---------------------------------------------------------------------------
-  // S tiles (row tile rt) in accumulator layout: rows 16 rt + 4 lq + e, column colw + l16.
-  f4 S[8];
+  // S tiles (tile j, row tile rt) in accumulator layout: rows 16 rt + 4 lq + e, column
+  // colw + 16 j + l16. Element (j, rt, e) sits at byte svo + (e PD + 16 j) 4 + 16 PD 4 rt of the
+  // head's 128 x 128 fp32 matrix: one lane offset, the rest in the instruction's immediate and
+  // scalar offsets (no per-element address registers). Without an init slot the buffer range
+  // is empty and every load returns 0; all loads are in flight together.
+  const int svo = ((4 * lq) * PD + colw + l16) * 4;
+  f4 S[TPW][8];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(P.state + (has_init ? (size_t)init * per + hoff : 0), has_init ? PD * PD * 4 : 0);
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + 4 * lq + e;
-      S[rt][e] = has_init ? P.state[init * per + hoff + (size_t)row * PD + colw + l16] : 0.f;
-    }
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S[j][rt][e] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, svo + (e * PD + 16 * j) * 4, rt * 16 * PD * 4, 0));
+  }
+  auto store_state = [&](int slot) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(P.state + (size_t)slot * per + hoff, PD * PD * 4);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[j][rt][e]), rd, svo + (e * PD + 16 * j) * 4,
+                                                rt * 16 * PD * 4, 0);
+  };
 
   for (int c = 0; c < nch; ++c) {
     const int n = min(PC, len - PC * c);
@@ -674,106 +698,138 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
     };
 
     // S -> B operands (channel blocks kk = 0..3); no LDS involved, ahead of the barrier
-    half8 sB[4], xB[2], wB[2];
+    half8 sB[TPW][4], xB[TPW][2], wB[TPW][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sB[kk] = acc_pair_to_b(S[2 * kk], S[2 * kk + 1]);
-    lds_barrier();   // BX: Kt and V of this chunk have landed
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sB[j][kk] = acc_pair_to_b(S[j][2 * kk], S[j][2 * kk + 1]);
+    lds_barrier();   // BX: -Kt and V of this chunk have landed
 
-    // Each phase issues all its LDS reads, then (past a scheduling fence, so the compiler cannot
-    // interleave them back into short load / wait / MFMA runs) its independent MFMA chains: the
-    // waits count down over reads that are all in flight.
-    // X = V - Kt S
-    f4 X[4], W[4];
+    // Every phase streams its fragments in small groups: the reads of group g + 1 are issued
+    // before the products of group g, with scheduling fences between, so the compiler neither
+    // hoists a whole phase's reads (register pressure) nor sinks them into short read / wait /
+    // product runs; each group's wait counts down over the reads issued after it.
+#define KDA_FENCE() __builtin_amdgcn_sched_barrier(0)
+    // X = V + (-Kt) S: the accumulators start from V; groups of four -Kt fragments (one
+    // channel block kk, all token tiles)
     {
-      half8 a[4][4];
-      uint32_t vv[4][4];
+      f4 X[TPW][4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) a[rt][kk] = frag(OFF_KT, 4 * rt + kk);
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+          for (int e = 0; e < 4; ++e)
+            X[j][rt][e] = __uint_as_float((uint32_t)vb[(16 * rt + 4 * lq + e) * VSW + cw + 16 * j + l16] << 16);
+      half8 a[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[rt][e] = vb[(16 * rt + 4 * lq + e) * VSW + cw + l16];
-      __builtin_amdgcn_sched_barrier(0);
+      for (int rt = 0; rt < 4; ++rt) a[0][rt] = frag(OFF_KT, 4 * rt);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) X[rt] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+          for (int rt = 0; rt < 4; ++rt) a[(kk + 1) & 1][rt] = frag(OFF_KT, 4 * rt + kk + 1);
+        }
+        KDA_FENCE();
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) X[rt] = mfma32(a[rt][kk], sB[kk], X[rt]);
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+          for (int j = 0; j < TPW; ++j) X[j][rt] = mfma32(a[kk & 1][rt], sB[j][kk], X[j][rt]);
+        KDA_FENCE();
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[rt][e] = __uint_as_float(vv[rt][e] << 16) - X[rt][e];
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) xB[j][kk] = acc_pair_to_b(X[j][2 * kk], X[j][2 * kk + 1]);
     }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) xB[kk] = acc_pair_to_b(X[2 * kk], X[2 * kk + 1]);
-    lds_barrier();   // BW: Qt, T and A_qk of this chunk have landed; Kt and V are free
+    lds_barrier();   // BW: Qt, T and A_qk of this chunk have landed; -Kt and V are free
 
     // W = T X (T is zero above the diagonal: token blocks kk <= rt / 2), then
     // O^T = S^T Qt^T + W^T A_qk^T: the operands of O = Qt S + A_qk W with their roles swapped.
-    // An accumulator tile then holds O[token 16 rt + l16][columns 4 lq .. 4 lq + 3 of the
-    // wave's tile], stored as 8 bf16 bytes; rows >= n fall outside the buffer range.
+    // An accumulator tile then holds O[token 16 rt + l16][columns 4 lq .. 4 lq + 3 of its
+    // 16-column tile], stored as 8 bf16 bytes; rows >= n fall outside the buffer range.
     {
-      half8 tf[6], b[4][4], q[6];
+      half8 tf[6], q[6], b[2][4];
 #pragma unroll
       for (int f = 0; f < 6; ++f) tf[f] = frag(OFF_T, f);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b[rt][kk] = frag(OFF_QT, 4 * rt + kk);
-#pragma unroll
       for (int f = 0; f < 6; ++f) q[f] = frag(OFF_AQ, f);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        W[rt] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 4; ++kk) b[0][kk] = frag(OFF_QT, kk);
+      KDA_FENCE();
 #pragma unroll
-        for (int kk = 0; kk <= rt / 2; ++kk) W[rt] = mfma32(tf[tri_frag(rt, kk)], xB[kk], W[rt]);
+      for (int j = 0; j < TPW; ++j) {
+        f4 W[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          W[rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk <= rt / 2; ++kk) W[rt] = mfma32(tf[tri_frag(rt, kk)], xB[j][kk], W[rt]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) wB[j][kk] = acc_pair_to_b(W[2 * kk], W[2 * kk + 1]);
       }
-      f4 O[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[rt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) O[rt] = mfma32(sB[kk], b[rt][kk], O[rt]);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) wB[kk] = acc_pair_to_b(W[2 * kk], W[2 * kk + 1]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int kk = 0; kk <= rt / 2; ++kk) O[rt] = mfma32(wB[kk], q[tri_frag(rt, kk)], O[rt]);
+      KDA_FENCE();
       const __amdgpu_buffer_rsrc_t ro =
           buffer_rsrc(A.t.o + (size_t)tok0 * H * PD + (size_t)h * PD + colw, (uint32_t)(n * hst2));
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const u2v ob = __builtin_bit_cast(u2v, __builtin_convertvector(O[rt], bf4));
-        __builtin_amdgcn_raw_buffer_store_b64(ob, ro, (16 * rt + l16) * hst2 + 8 * lq, 0, 0);
+        if (rt < 3) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) b[(rt + 1) & 1][kk] = frag(OFF_QT, 4 * (rt + 1) + kk);
+        }
+        KDA_FENCE();
+        f4 O[TPW];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) O[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) O[j] = mfma32(sB[j][kk], b[rt & 1][kk], O[j]);
+#pragma unroll
+        for (int kk = 0; kk <= rt / 2; ++kk)
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) O[j] = mfma32(wB[j][kk], q[tri_frag(rt, kk)], O[j]);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          const u2v ob = __builtin_bit_cast(u2v, __builtin_convertvector(O[j], bf4));
+          __builtin_amdgcn_raw_buffer_store_b64(ob, ro, (16 * rt + l16) * hst2 + 32 * j + 8 * lq, 0, 0);
+        }
+        KDA_FENCE();
       }
     }
     lds_barrier();   // BS: Kbar^T and 2^(G_C) of this chunk have landed; Qt, T, A_qk are free
 
-    // S <- Diag(2^(G_C)) S + Kbar^T W
+    // S <- Diag(2^(G_C)) S + Kbar^T W, in groups of two channel tiles
     {
       const float* gam = reinterpret_cast<const float*>(buf + OFF_GAM);
-      half8 kb[8][2];
-      f4 g[8];
+      half8 kb[2][4];
+      f4 g[2][2];
+      auto rd = [&](int gi, half8* kbp, f4* gp) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+        for (int i = 0; i < 4; ++i) kbp[i] = frag(OFF_KB, 4 * gi + i);   // channel tiles 2gi, 2gi+1
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) kb[rt][kk] = frag(OFF_KB, 2 * rt + kk);
+        for (int i = 0; i < 2; ++i) gp[i] = *reinterpret_cast<const f4*>(gam + 16 * (2 * gi + i) + 4 * lq);
+      };
+      rd(0, kb[0], g[0]);
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt) g[rt] = *reinterpret_cast<const f4*>(gam + 16 * rt + 4 * lq);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int gi = 0; gi < 4; ++gi) {
+        if (gi < 3) rd(gi + 1, kb[(gi + 1) & 1], g[(gi + 1) & 1]);
+        KDA_FENCE();
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt) S[rt] *= g[rt];
+        for (int i = 0; i < 2; ++i) {
+          const int rt = 2 * gi + i;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+          for (int j = 0; j < TPW; ++j) {
+            S[j][rt] *= g[gi & 1][i];
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) S[rt] = mfma32(kb[rt][kk], wB[kk], S[rt]);
+            for (int kk = 0; kk < 2; ++kk) S[j][rt] = mfma32(kb[gi & 1][2 * i + kk], wB[j][kk], S[j][rt]);
+          }
+        }
+        KDA_FENCE();
+      }
     }
+#undef KDA_FENCE
 
     // ---- checkpoint export inside the pass -------------------------------------------------
     const int done = PC * c + n;
@@ -783,13 +839,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
       typedef const __attribute__((address_space(4))) int32_t* cptr;
       const int dst = ((cptr)(uintptr_t)A.ckpt_slot)[ck++];
       if (dst >= 0 && dst < P.num_slots) {
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = 16 * rt + 4 * lq + e;
-            P.state[dst * per + hoff + (size_t)row * PD + colw + l16] = S[rt][e];
-          }
+        store_state(dst);
         if (t == 0 && h == 0 && vs == 0) {
           kda_slot_meta mm{pos0 + done, 0, 0, 0, 0};
           P.meta[dst] = mm;
@@ -801,13 +851,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   const int out = A.out_slot[si];
   if (out >= 0 && out < P.num_slots) {
     __syncthreads();   // the init slot may be the out slot: every read of it is done
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * rt + 4 * lq + e;
-        P.state[out * per + hoff + (size_t)row * PD + colw + l16] = S[rt][e];
-      }
+    store_state(out);
     if (t == 0 && h == 0 && vs == 0) {
       kda_slot_meta mm{pos0 + len, 0, 0, 0, 0};
       P.meta[out] = mm;
@@ -831,13 +875,18 @@ int device_cu_count() {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
 
-template <int CW, int LW>
+template <int CW, int TPW, int LW>
 hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
                         const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
   const int n_hg = a.n_seq * p.H;
-  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (16 * CW));
-  hipLaunchKernelGGL((state_pass_kernel<CW, LW>), dim3(nb), dim3(64 * (CW + LW)), 0, s, p, a, choff,
-                     ckoff, order, blocks, n_hg);
+  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (16 * CW * TPW));
+  // The rest of the CU's LDS is requested too (unused), so that no other work-group shares a CU
+  // with a state-pass work-group: in a mixed batch the decode and verify kernels on the side
+  // stream then run on the CUs the pass leaves free instead of slowing its sequential chain.
+  constexpr int lds_static = 2 * StateBuf<16 * CW * TPW, 64 * LW>::BYTES;
+  static_assert(lds_static <= LDS_PER_CU, "state pass LDS image");
+  hipLaunchKernelGGL((state_pass_kernel<CW, TPW, LW>), dim3(nb), dim3(64 * (CW + LW)),
+                     LDS_PER_CU - lds_static, s, p, a, choff, ckoff, order, blocks, n_hg);
   return hipGetLastError();
 }
 
@@ -881,9 +930,9 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
   // with fewer compute waves per CU (less LDS traffic each), while more work-groups per head
   // only pay off while CUs would otherwise idle. Larger batches take 64-column slices.
   const int n_hg = a.n_seq * p.H, cus = device_cu_count();
-  if (n_hg * 8 <= cus) return launch_state<1, 2>(p, a, choff, ckoff, order, blocks, s);
-  if (n_hg * 4 <= cus) return launch_state<2, 2>(p, a, choff, ckoff, order, blocks, s);
-  return launch_state<4, 4>(p, a, choff, ckoff, order, blocks, s);
+  if (n_hg * 8 <= cus) return launch_state<1, 1, 4>(p, a, choff, ckoff, order, blocks, s);
+  if (n_hg * 4 <= cus) return launch_state<2, 1, 4>(p, a, choff, ckoff, order, blocks, s);
+  return launch_state<4, 1, 4>(p, a, choff, ckoff, order, blocks, s);
 }
 
 }  // namespace kda
