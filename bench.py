@@ -12,7 +12,10 @@ chunk_prep and state_pass kernels), timed with HIP events on the stream the libr
 on, in a second timed pass that issues the same calls one by one. `cpu_baseline` times the CPU
 oracle on a bounded sample (a subset of heads).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 30]
+
+The warm-up steps bring the GPU to its steady clock (the first few dozen steps after start run
+~5% slower); the timed steps then measure the steady serving rate.
 """
 from __future__ import annotations
 
@@ -124,8 +127,8 @@ def cpu_baseline(w, heads: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
