@@ -82,6 +82,16 @@ def verify_bytes(B, P, H):
     return B * H * (STATE_B + P * (TOK_IN_B + TOK_OUT_B + RING_ENTRY_B))
 
 
+def verify_direct_bytes(B, P, H):
+    """Direct per-draft checkpoints: the verify's state read and token traffic plus one state
+    write per position (in place of the ring entries)."""
+    return B * H * (STATE_B + P * (TOK_IN_B + TOK_OUT_B) + P * STATE_B)
+
+
+def commit_direct_bytes(B, H):
+    return B * H * 2 * STATE_B
+
+
 def commit_bytes(n_replayed_total, B, H):
     return B * H * 2 * STATE_B + n_replayed_total * H * RING_ENTRY_B
 
@@ -200,8 +210,11 @@ def main():
     vq, vk, vv, va, vb, vo = (sl(t, n_pre + nd, total_tok).reshape((nv, P) + t.shape[1:])
                               for t in (q, k, v, a, b, o))
     pq, pk, pv, pa, pb, po = (sl(t, 0, n_pre) for t in (q, k, v, a, b, o))
-    names = ["prefill", "decode", "verify", "commit"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # ... and the direct per-draft checkpoint pair on the same verify slots, the scheme
+    # ReplaySSM is weighed against (state written at every verified position)
+    names = ["prefill", "decode", "verify", "commit", "verify_direct", "commit_direct"]
+    draft = pool.kda_draft_states(nv, P)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for s in range(args.steps):
         E = ev[s]
         E[0].record()
@@ -213,12 +226,17 @@ def main():
         E[3].record()
         pool.kda_commit(i_vs, na)
         E[4].record()
+        pool.kda_verify_direct(vq, vk, vv, va, vb, i_vs, draft_states=draft, o=vo)
+        E[5].record()
+        pool.kda_commit_direct(i_vs, na, draft)
+        E[6].record()
     torch.cuda.synchronize()
     ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
           for i, n in enumerate(names)}
     n_rep = int(np.sum(1 + w["n_accepted"]))
     byts = {"prefill": prefill_bytes(n_pre, H, len(ps)), "decode": decode_bytes(nd, H),
-            "verify": verify_bytes(nv, P, H), "commit": commit_bytes(n_rep, nv, H)}
+            "verify": verify_bytes(nv, P, H), "commit": commit_bytes(n_rep, nv, H),
+            "verify_direct": verify_direct_bytes(nv, P, H), "commit_direct": commit_direct_bytes(nv, H)}
     kernels = {n: {"ms": round(ms[n], 5), "alg_bytes": byts[n],
                    "GBps": round(byts[n] / ms[n] / 1e6, 1),
                    "hbm_frac": round(byts[n] / ms[n] / 1e6 / HBM_PEAK_GBS, 4)} for n in names}

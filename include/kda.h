@@ -177,6 +177,28 @@ kda_status kda_commit(kda_pool* pool, int32_t B, const int32_t* h_slots,
 kda_status kda_rollback(kda_pool* pool, int32_t B, const int32_t* h_slots,
                         const int32_t* d_slots, void* stream);
 
+/* ---- direct per-draft state checkpoints (the alternative ReplaySSM is weighed against) ---
+ * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "ReplaySSM shrinks rollback state":
+ * the scheme that saves the state at every drafted position, against which the ring is the
+ * smaller one.) kda_verify_direct is kda_verify except that, instead of appending ring
+ * entries, it writes the state after each of its n_pos positions to draft_states
+ * ([B][n_pos][H][dk][dv] fp32, device, 16-byte aligned, caller-owned,
+ * kda_draft_state_bytes(...) bytes). Outputs o are bit-identical to kda_verify's. The ring is
+ * untouched; the slot becomes pending a direct commit (v_base = ring_head, v_npos = pending =
+ * n_pos); 1 <= n_pos <= ring_cap as for kda_verify. kda_commit_direct then copies
+ * draft_states[b][n] (n = d_n_accepted[b], clamped to [0, v_npos - 1] with
+ * KDA_DEVERR_NACC_RANGE as in kda_commit) into the slot: the same state kda_commit would
+ * build by replay, bit for bit; pos += 1 + n, pending = 0, ring_head unchanged. The commit
+ * takes the same draft_states buffer, n_pos and slot order as the verify (EINVAL otherwise);
+ * kda_commit refuses slots pending a direct commit and kda_commit_direct slots pending a
+ * ring commit (ESTATE); kda_rollback clears either. Draft buffers stay the caller's.     */
+size_t kda_draft_state_bytes(const kda_pool_desc* desc, int32_t B, int32_t n_pos);
+kda_status kda_verify_direct(kda_pool* pool, const kda_step_args* args, int32_t n_pos,
+                             void* draft_states, void* stream);
+kda_status kda_commit_direct(kda_pool* pool, int32_t B, const int32_t* h_slots,
+                             const int32_t* d_slots, const int32_t* d_n_accepted,
+                             const void* draft_states, int32_t n_pos, void* stream);
+
 /* ---- mixed speculative / non-speculative batch ---------------------------------------
  * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "Small tensor copies leave the hot
  * path": contiguous zero-copy slices and direct output writes instead of index_select /
@@ -209,7 +231,8 @@ kda_status kda_read_device_error(kda_pool* pool, uint32_t* bits_out, void* strea
 const char* kda_status_string(kda_status status);
 const char* kda_last_error(void);
 
-/* Host-side view of a slot: 0 free, 1 idle, 2 pending; -1 for an id out of range.          */
+/* Host-side view of a slot: 0 free, 1 idle, 2 pending a ring commit, 3 pending a direct
+ * commit; -1 for an id out of range.                                                      */
 int32_t kda_slot_host_state(const kda_pool* pool, int32_t slot);
 
 #ifdef __cplusplus

@@ -79,6 +79,10 @@ PROTOTYPES = {
     "kda_verify": (c_int32, [c_void_p, POINTER(kda_step_args), c_int32, c_void_p]),
     "kda_commit": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "kda_rollback": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "kda_draft_state_bytes": (c_size_t, [POINTER(kda_pool_desc), c_int32, c_int32]),
+    "kda_verify_direct": (c_int32, [c_void_p, POINTER(kda_step_args), c_int32, c_void_p, c_void_p]),
+    "kda_commit_direct": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_int32, c_void_p]),
     "kda_mixed_batch": (c_int32, [c_void_p, POINTER(kda_mixed_args), c_void_p]),
     "kda_read_device_error": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
     "kda_status_string": (c_char_p, [c_int32]),
@@ -102,7 +106,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"KDA HIP library not found at {path}; build it with "
-            "`python -m recurrent_linear_attention_amd.build` (there is no CPU fallback)")
+            "`python recurrent_linear_attention_amd/build.py` (there is no CPU fallback)")
     lib = ctypes.CDLL(path)
     _check_single_runtime()
     for name, (res, args) in PROTOTYPES.items():

@@ -1,6 +1,8 @@
 """Build the KDA HIP library (libkda.so) in-tree for gfx950 with hipcc.
 
-    python -m recurrent_linear_attention_amd.build
+    python recurrent_linear_attention_amd/build.py
+
+(Run as a script: importing it through the package would first load the library it builds.)
 """
 from __future__ import annotations
 

@@ -47,6 +47,13 @@ hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots,
                          const int32_t* d_n_accepted, hipStream_t s);
 hipError_t launch_rollback(const PoolView& p, int32_t B, const int32_t* d_slots,
                            hipStream_t s);
+// Direct per-draft checkpoints: verify writes every position's state to draft
+// ([B][n_pos][H][dk][dv] fp32); commit copies draft[b][n_accepted[b]] into the slot.
+hipError_t launch_verify_direct(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
+                                const int32_t* d_slots, float* draft, hipStream_t s);
+hipError_t launch_commit_direct(const PoolView& p, int32_t B, const int32_t* d_slots,
+                                const int32_t* d_n_acc, const float* draft, int32_t n_pos,
+                                hipStream_t s);
 hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s);
 hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t s);

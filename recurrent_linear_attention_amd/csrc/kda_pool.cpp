@@ -35,7 +35,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-enum : uint8_t { SLOT_FREE = 0, SLOT_IDLE = 1, SLOT_PENDING = 2 };
+// Host slot states; SLOT_ANY_PENDING is only a check argument (either pending state).
+enum : uint8_t { SLOT_FREE = 0, SLOT_IDLE = 1, SLOT_PENDING = 2, SLOT_PENDING_DIRECT = 3, SLOT_ANY_PENDING = 4 };
 
 kda_status check_desc(const kda_pool_desc* d) {
   if (!d) return fail(KDA_EINVAL, "null pool descriptor");
@@ -61,7 +62,10 @@ void ring_offsets(const kda_pool_desc* d, size_t off[4], size_t* total) {
 struct kda_pool {
   kda_pool_desc desc;
   kda::PoolView view;
-  std::vector<uint8_t> slot_state;     // SLOT_FREE / SLOT_IDLE / SLOT_PENDING
+  std::vector<uint8_t> slot_state;     // SLOT_FREE / SLOT_IDLE / SLOT_PENDING / SLOT_PENDING_DIRECT
+  // Direct verify of a slot pending a direct commit: its draft buffer, n_pos and batch index.
+  std::vector<const void*> draft_buf;
+  std::vector<int32_t> draft_npos, draft_index;
   std::vector<uint32_t> stamp;         // distinctness checks
   uint32_t epoch = 0;
   void* ws = nullptr;                  // prefill workspace used when the caller passes none
@@ -97,9 +101,13 @@ kda_status check_slots(kda_pool* p, int32_t B, const int32_t* h, uint8_t want,
     int32_t s = h[i];
     if (s < 0 || s >= p->desc.num_slots || p->slot_state[s] == SLOT_FREE)
       return fail(KDA_EINVAL, "slot %d (entry %d) is not a live slot", s, i);
-    if (p->slot_state[s] != want)
+    const uint8_t st = p->slot_state[s];
+    const bool ok = want == SLOT_ANY_PENDING ? (st == SLOT_PENDING || st == SLOT_PENDING_DIRECT) : st == want;
+    if (!ok)
       return fail(KDA_ESTATE, "slot %d is %s", s,
-                  p->slot_state[s] == SLOT_PENDING ? "pending a verify" : "not pending");
+                  st == SLOT_PENDING          ? "pending a ring commit (kda_commit / kda_rollback)"
+                  : st == SLOT_PENDING_DIRECT ? "pending a direct commit (kda_commit_direct / kda_rollback)"
+                                              : "not pending");
     if (!p->mark(s)) return fail(KDA_EINVAL, "slot %d repeats within one call", s);
   }
   return KDA_OK;
@@ -129,6 +137,11 @@ extern "C" {
 size_t kda_state_bytes(const kda_pool_desc* d) {
   if (check_desc(d) != KDA_OK) return 0;
   return (size_t)d->num_slots * d->num_heads * d->dk * d->dv * sizeof(float);
+}
+
+size_t kda_draft_state_bytes(const kda_pool_desc* d, int32_t B, int32_t n_pos) {
+  if (check_desc(d) != KDA_OK || B < 0 || n_pos < 0) return 0;
+  return (size_t)B * n_pos * d->num_heads * d->dk * d->dv * sizeof(float);
 }
 
 size_t kda_ring_bytes(const kda_pool_desc* d) {
@@ -184,6 +197,9 @@ kda_status kda_pool_create(const kda_pool_desc* d, void* state, void* ring, void
   p->view.dv = d->dv;
   p->view.R = d->ring_cap;
   p->slot_state.assign(d->num_slots, SLOT_FREE);
+  p->draft_buf.assign(d->num_slots, nullptr);
+  p->draft_npos.assign(d->num_slots, 0);
+  p->draft_index.assign(d->num_slots, 0);
   p->stamp.assign(d->num_slots, 0u);
   *out = p;
   return KDA_OK;
@@ -216,7 +232,8 @@ kda_status kda_slot_free(kda_pool* p, int32_t s) {
   if (!p) return fail(KDA_EINVAL, "null pool");
   if (s < 0 || s >= p->desc.num_slots || p->slot_state[s] == SLOT_FREE)
     return fail(KDA_EINVAL, "slot %d is not live", s);
-  if (p->slot_state[s] == SLOT_PENDING) return fail(KDA_ESTATE, "slot %d is pending", s);
+  if (p->slot_state[s] == SLOT_PENDING || p->slot_state[s] == SLOT_PENDING_DIRECT)
+    return fail(KDA_ESTATE, "slot %d is pending", s);
   p->slot_state[s] = SLOT_FREE;
   return KDA_OK;
 }
@@ -409,7 +426,7 @@ kda_status kda_commit(kda_pool* p, int32_t B, const int32_t* h_slots, const int3
 kda_status kda_rollback(kda_pool* p, int32_t B, const int32_t* h_slots, const int32_t* d_slots,
                         void* stream) {
   if (!p) return fail(KDA_EINVAL, "null pool");
-  kda_status st = check_slots(p, B, h_slots, SLOT_PENDING);
+  kda_status st = check_slots(p, B, h_slots, SLOT_ANY_PENDING);
   if (st != KDA_OK) return st;
   if (B == 0) return KDA_OK;
   if (!d_slots) return fail(KDA_EINVAL, "null device slot array");
@@ -518,6 +535,56 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "mixed: decode / verify launch");
   }
   for (int32_t i = 0; i < m->n_verify; ++i) p->slot_state[m->h_verify_slots[i]] = SLOT_PENDING;
+  return KDA_OK;
+}
+
+kda_status kda_verify_direct(kda_pool* p, const kda_step_args* a, int32_t n_pos, void* draft,
+                             void* stream) {
+  if (!p || !a) return fail(KDA_EINVAL, "null argument");
+  if (n_pos < 1 || n_pos > p->desc.ring_cap)
+    return fail(KDA_EINVAL, "n_pos %d outside 1..ring_cap (%d)", n_pos, p->desc.ring_cap);
+  kda_status st = check_slots(p, a->B, a->h_slots, SLOT_IDLE);
+  if (st != KDA_OK) return st;
+  if (a->B == 0) return KDA_OK;
+  st = check_tensors(a->q, a->k, a->v, a->a, a->b, a->o);
+  if (st != KDA_OK) return st;
+  if (!a->d_slots) return fail(KDA_EINVAL, "null device slot array");
+  if (!draft || !aligned(draft, 16)) return fail(KDA_EINVAL, "draft states must be 16-byte aligned");
+  hipError_t e = kda::launch_verify_direct(p->view, tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->B,
+                                           n_pos, a->d_slots, static_cast<float*>(draft), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "direct verify launch");
+  for (int32_t i = 0; i < a->B; ++i) {
+    const int32_t s = a->h_slots[i];
+    p->slot_state[s] = SLOT_PENDING_DIRECT;
+    p->draft_buf[s] = draft;
+    p->draft_npos[s] = n_pos;
+    p->draft_index[s] = i;
+  }
+  return KDA_OK;
+}
+
+kda_status kda_commit_direct(kda_pool* p, int32_t B, const int32_t* h_slots, const int32_t* d_slots,
+                             const int32_t* d_n_accepted, const void* draft, int32_t n_pos,
+                             void* stream) {
+  if (!p) return fail(KDA_EINVAL, "null pool");
+  kda_status st = check_slots(p, B, h_slots, SLOT_PENDING_DIRECT);
+  if (st != KDA_OK) return st;
+  if (B == 0) return KDA_OK;
+  if (!d_slots || !d_n_accepted) return fail(KDA_EINVAL, "null device array");
+  for (int32_t i = 0; i < B; ++i) {
+    const int32_t s = h_slots[i];
+    if (p->draft_buf[s] != draft || p->draft_npos[s] != n_pos || p->draft_index[s] != i)
+      return fail(KDA_EINVAL,
+                  "slot %d (entry %d): draft buffer, n_pos and slot order must match its direct "
+                  "verify (entry %d, n_pos %d)", s, i, p->draft_index[s], p->draft_npos[s]);
+  }
+  hipError_t e = kda::launch_commit_direct(p->view, B, d_slots, d_n_accepted,
+                                           static_cast<const float*>(draft), n_pos, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "direct commit launch");
+  for (int32_t i = 0; i < B; ++i) {
+    p->slot_state[h_slots[i]] = SLOT_IDLE;
+    p->draft_buf[h_slots[i]] = nullptr;
+  }
   return KDA_OK;
 }
 

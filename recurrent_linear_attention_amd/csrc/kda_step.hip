@@ -284,6 +284,80 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, cons
   }
 }
 
+// Direct per-draft state checkpointing, the scheme ReplaySSM is weighed against ("vLLM lifts
+// Kimi K3 throughput by up to 2.8x", section "ReplaySSM shrinks rollback state"): verify
+// writes the state after every position j to draft[bi][j] ([B][n_pos][H][D][D] fp32) instead
+// of appending ring entries; the outputs are those of verify_kernel (same step code, same
+// order). The ring is untouched.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void verify_direct_kernel(PoolView P, StepTensors T, int n_pos,
+                                                                       const int32_t* __restrict__ slots,
+                                                                       float* __restrict__ draft) {
+  using C = StepCfg<D>;
+  __shared__ StepLds<C> lds;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
+  float S[C::RPT][4];
+  load_state<C>(S, Sp, r0, c0);
+  for (int j = 0; j < n_pos; ++j) {
+    const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
+    StepIn<C> in;
+    load_in<C, true>(in, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+    float o[4];
+    step<C, true>(S, in, lds, j & 1, o);
+    if (rg == 0) {
+      uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+      store_bf16_raw<4>(T.o + row * D + c0, ow);
+    }
+    store_state<C>(S, draft + row * D * D, r0, c0);
+  }
+  if (t == 0 && h == 0 && vs == 0) {
+    P.meta[slot].v_base = wrap(P.meta[slot].ring_head, P.R);
+    P.meta[slot].v_npos = n_pos;
+    P.meta[slot].pending = n_pos;
+  }
+}
+
+// Direct commit: the slot's state becomes draft[bi][n_accepted] (the state after 1 +
+// n_accepted positions); pos advances by 1 + n_accepted, the ring pointer stays. n_accepted
+// outside [0, v_npos - 1] is clamped and flagged as in commit_kernel.
+template <int D>
+__global__ __launch_bounds__(StepCfg<D>::NT) void commit_direct_kernel(PoolView P, const int32_t* __restrict__ slots,
+                                                                       const int32_t* __restrict__ n_acc,
+                                                                       const float* __restrict__ draft, int n_pos) {
+  using C = StepCfg<D>;
+  constexpr int NVS = D / C::VS;
+  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  int vn = P.meta[slot].v_npos;
+  vn = vn < 1 ? 1 : (vn > n_pos ? n_pos : vn);
+  int na = n_acc[bi];
+  const bool bad = na < 0 || na > vn - 1;
+  na = na < 0 ? 0 : (na > vn - 1 ? vn - 1 : na);
+  float S[C::RPT][4];
+  load_state<C>(S, draft + (((size_t)bi * n_pos + na) * P.H + h) * D * D, r0, c0);
+  store_state<C>(S, P.state + ((size_t)slot * P.H + h) * D * D, r0, c0);
+  if (t == 0 && h == 0 && vs == 0) {
+    P.meta[slot].pos += 1 + na;
+    P.meta[slot].pending = 0;
+    if (bad) atomicOr(P.err, (uint32_t)KDA_DEVERR_NACC_RANGE);
+  }
+}
+
 // Recurrent-form prefill: one work-group per (sequence, head, value slice) walks its
 // sequence token by token with the decode step, exporting the state at every checkpoint
 // boundary inside the same pass and the final state at the end.
@@ -401,6 +475,28 @@ hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots, c
     hipLaunchKernelGGL(commit_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, d_slots, d_n_acc);
   else
     hipLaunchKernelGGL(commit_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, d_slots, d_n_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_direct(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
+                                const int32_t* d_slots, float* draft, hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(verify_direct_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, t,
+                       n_pos, d_slots, draft);
+  else
+    hipLaunchKernelGGL(verify_direct_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, t,
+                       n_pos, d_slots, draft);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_direct(const PoolView& p, int32_t B, const int32_t* d_slots, const int32_t* d_n_acc,
+                                const float* draft, int32_t n_pos, hipStream_t s) {
+  if (p.dk == 128)
+    hipLaunchKernelGGL(commit_direct_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p,
+                       d_slots, d_n_acc, draft, n_pos);
+  else
+    hipLaunchKernelGGL(commit_direct_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p,
+                       d_slots, d_n_acc, draft, n_pos);
   return hipGetLastError();
 }
 

@@ -29,6 +29,13 @@ def _stream(stream=None) -> c_void_p:
     return c_void_p(s.cuda_stream)
 
 
+def _check_draft(t: torch.Tensor, B: int, n_pos: int, H: int, d: int) -> None:
+    if (t.dtype != torch.float32 or not t.is_contiguous() or t.device.type != "cuda"
+            or tuple(t.shape) != (B, n_pos, H, d, d)):
+        raise ValueError(f"draft_states must be a contiguous float32 device tensor of shape "
+                         f"{(B, n_pos, H, d, d)}")
+
+
 def _dev(t: torch.Tensor | None, dtype, name: str) -> int | None:
     if t is None:
         return None
@@ -194,6 +201,40 @@ class KDAPool:
         na = _dev(n_accepted, torch.int32, "n_accepted")
         check(lib.kda_commit(self.handle, s.np.size, s.h, s.d, na, _stream(stream)),
               "kda_commit")
+
+    def kda_draft_states(self, B: int, n_pos: int) -> torch.Tensor:
+        """A draft-state buffer for kda_verify_direct: fp32 [B, n_pos, H, d, d] on the pool's
+        device (kda_draft_state_bytes bytes)."""
+        n = lib.kda_draft_state_bytes(byref(self.desc), B, n_pos)
+        if n == 0 and B * n_pos > 0:
+            raise ValueError("invalid draft-state geometry")
+        return torch.empty((B, n_pos, self.H, self.d, self.d), dtype=torch.float32, device=self.device)
+
+    def kda_verify_direct(self, q, k, v, a, b, slots, draft_states=None, o=None, stream=None):
+        """Verify P positions per sequence, writing the state after every position to
+        draft_states [B, P, H, d, d] (allocated when None) instead of the ring. Returns
+        (o, draft_states)."""
+        n_pos = q.shape[1]
+        if o is None:
+            o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
+        if draft_states is None:
+            draft_states = self.kda_draft_states(q.shape[0], n_pos)
+        _check_draft(draft_states, q.shape[0], n_pos, self.H, self.d)
+        args, keep = self._step_args(q, k, v, a, b, o, slots)
+        check(lib.kda_verify_direct(self.handle, byref(args), n_pos, draft_states.data_ptr(),
+                                    _stream(stream)), "kda_verify_direct")
+        return o, draft_states
+
+    def kda_commit_direct(self, slots, n_accepted: torch.Tensor, draft_states: torch.Tensor,
+                          stream=None) -> None:
+        """Commit by copying draft_states[b, n_accepted[b]] (the buffer, position count and slot
+        order of the kda_verify_direct call) into each slot."""
+        s = _ix(slots, self.device)
+        na = _dev(n_accepted, torch.int32, "n_accepted")
+        n_pos = draft_states.shape[1]
+        _check_draft(draft_states, s.np.size, n_pos, self.H, self.d)
+        check(lib.kda_commit_direct(self.handle, s.np.size, s.h, s.d, na, draft_states.data_ptr(),
+                                    n_pos, _stream(stream)), "kda_commit_direct")
 
     def kda_rollback(self, slots, stream=None) -> None:
         s = _ix(slots, self.device)

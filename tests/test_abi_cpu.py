@@ -14,7 +14,11 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "recurrent_linear_attention_amd", "lib", "libkda.so")
 if not os.path.exists(LIB):   # the library is built, not committed
-    from recurrent_linear_attention_amd import build as _b
+    import importlib.util   # build.py from its file: the package __init__ loads the library
+    _spec = importlib.util.spec_from_file_location(
+        "_kda_build", os.path.join(ROOT, "recurrent_linear_attention_amd", "build.py"))
+    _b = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(_b)
     _b.build()
 
 from recurrent_linear_attention_amd import _abi  # noqa: E402
@@ -54,8 +58,11 @@ def test_size_helpers():
     assert lib.kda_meta_error_offset(byref(d)) >= 256 * 24
     assert lib.kda_meta_bytes(byref(d)) >= lib.kda_meta_error_offset(byref(d)) + 4
     assert ctypes.sizeof(_abi.kda_slot_meta) == 24
+    assert lib.kda_draft_state_bytes(byref(d), 4, 9) == 4 * 9 * 32 * 128 * 128 * 4
+    assert lib.kda_draft_state_bytes(byref(d), -1, 9) == 0
     bad = _abi.kda_pool_desc(8, 2, 64, 64, 9)
     assert lib.kda_state_bytes(byref(bad)) == 0          # d = 64 not instantiated
+    assert lib.kda_draft_state_bytes(byref(bad), 1, 1) == 0
 
 
 class HostPool:
@@ -145,6 +152,25 @@ def test_step_validation_errors_launch_nothing():
     assert lib.kda_decode(p.h, byref(step_args(0, ok)), None) == 0
     assert lib.kda_slot_reset(p.h, 7, None) == _abi.KDA_EINVAL
     assert lib.kda_slot_checkpoint(p.h, s0, s0, None) == _abi.KDA_EINVAL
+
+
+def test_direct_checkpoint_validation_errors_launch_nothing():
+    p = HostPool()
+    s0, s1 = p.alloc()[1], p.alloc()[1]
+    ok = i32(s0, s1)
+    # n_pos outside 1..ring_cap, missing / misaligned draft buffer
+    assert lib.kda_verify_direct(p.h, byref(step_args(2, ok)), 10, FAKE, None) == _abi.KDA_EINVAL
+    assert lib.kda_verify_direct(p.h, byref(step_args(2, ok)), 0, FAKE, None) == _abi.KDA_EINVAL
+    assert lib.kda_verify_direct(p.h, byref(step_args(2, ok)), 3, None, None) == _abi.KDA_EINVAL
+    assert lib.kda_verify_direct(p.h, byref(step_args(2, ok)), 3, FAKE + 4, None) == _abi.KDA_EINVAL
+    dup = i32(s0, s0)
+    assert lib.kda_verify_direct(p.h, byref(step_args(2, dup)), 3, FAKE, None) == _abi.KDA_EINVAL
+    # a direct commit of idle slots: wrong state
+    assert lib.kda_commit_direct(p.h, 2, ok.ctypes.data, FAKE, FAKE, FAKE, 3, None) == _abi.KDA_ESTATE
+    assert b"not pending" in lib.kda_last_error()
+    # nothing changed host-side; zero-size batches are no-ops
+    assert lib.kda_slot_host_state(p.h, s0) == 1 and lib.kda_slot_host_state(p.h, s1) == 1
+    assert lib.kda_verify_direct(p.h, byref(step_args(0, ok)), 3, FAKE, None) == 0
 
 
 def prefill_args(cu, out, init=None, ckpt=None, chunk=16, interval=0):

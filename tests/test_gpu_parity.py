@@ -161,6 +161,63 @@ def test_verify_commit_rollback_full_size():
     assert g.kda_read_device_error() == 0
 
 
+@pytest.mark.parametrize("d", [128, 16])
+def test_direct_per_draft_checkpoints_match_ring_scheme(d):
+    """Direct per-draft state checkpoints beside ReplaySSM: the same outputs as the ring
+    verify (bit for bit), draft states equal to the oracle's prefix states, and a direct
+    commit that leaves the same state bytes as the ring commit's replay; the ring pointer stays.
+    Out-of-range acceptance is clamped and flagged; the two pending kinds do not mix."""
+    w = ki.verify_workload(2) if d == 128 else ki.verify_workload(7, B=3, P=5, H=2, d=16, n_slots=8)
+    P = w["n_pos"]
+    g, o = pools(w["n_slots"], w["H"], w["dk"], w["ring_cap"])
+    r, _ = pools(w["n_slots"], w["H"], w["dk"], w["ring_cap"])
+    slots = w["slots"]
+    put_states(g, o, slots, w["states"])
+    r.state.copy_(g.state)
+    tok = w["tokens"]
+    before = g.state.clone()
+    meta_before = g.meta_array().copy()
+    O, draft = g.kda_verify_direct(*tok_dev(tok), slots)
+    Or = r.kda_verify(*tok_dev(tok), slots)
+    Oo, states_o = o.verify_direct(tok.np, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Or), "direct verify outputs must equal the ring verify's"
+    assert rel_bf16(O, Oo) <= TOL
+    assert rel(draft, states_o) <= TOL
+    assert torch.equal(g.state, before), "direct verify must not write any committed state"
+    meta_equal(g.meta_array(), o.meta(), slots)
+    assert all(g.host_state(int(s)) == 3 for s in slots)
+    with pytest.raises(kda.KDAError):           # a ring commit of a slot pending a direct one
+        g.kda_commit(slots, torch.zeros(len(slots), dtype=torch.int32, device="cuda"))
+
+    na_np = w["n_accepted"].copy()
+    na_np[-1] = P + 3                           # out of range: clamped to P - 1 and flagged
+    na = torch.from_numpy(na_np).to("cuda")
+    g.kda_commit_direct(slots, na, draft)
+    r.kda_commit(slots, na)
+    o.commit_direct(slots, na_np, states_o)
+    torch.cuda.synchronize()
+    assert torch.equal(g.state, r.state), "direct commit must leave the ring commit's state bytes"
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+    m, mr = g.meta_array(), r.meta_array()
+    assert np.array_equal(m[slots, 0], mr[slots, 0])                   # pos advanced alike
+    assert np.array_equal(m[slots, 1], meta_before[slots, 1])          # ring_head unchanged
+    assert g.kda_read_device_error() == 1 and r.kda_read_device_error() == 1
+
+    # a full reject after a direct verify: state bit-identical, pointers untouched
+    snap, msnap = g.state.clone(), g.meta_array().copy()
+    g.kda_verify_direct(*tok_dev(tok), slots, draft_states=draft)
+    g.kda_rollback(slots)
+    torch.cuda.synchronize()
+    assert torch.equal(g.state, snap)
+    m = g.meta_array()
+    assert np.array_equal(m[slots, :3], np.stack([msnap[slots, 0], msnap[slots, 1],
+                                                  np.zeros(len(slots), np.int64)], axis=1))
+    assert all(g.host_state(int(s)) == 1 for s in slots)
+    assert g.kda_read_device_error() == 0
+
+
 def test_commit_out_of_range_acceptance_is_clamped_and_flagged():
     w = ki.verify_workload(5, B=2, P=4)
     g, o = pools(16, w["H"], w["dk"], 9)

@@ -262,6 +262,70 @@ def test_commit_clamps_out_of_range_acceptance():
     assert tuple(p.meta()[s])[:3] == (3, 3, 0)
 
 
+def test_direct_checkpoints_are_the_prefix_states():
+    """Direct per-draft checkpoints: the state kept for position j is the sequential scan's
+    state after positions 0..j, and the outputs are the ring verify's."""
+    rng = np.random.default_rng(21)
+    H, d, P = 2, 8, 5
+    p, r = KDAPool(3, H, d, d, 9), KDAPool(3, H, d, d, 9)
+    slots = [p.alloc(), p.alloc()]
+    assert [r.alloc(), r.alloc()] == slots
+    S0 = rng.standard_normal((2, H, d, d))
+    p.state[slots] = S0
+    r.state[slots] = S0
+    tok = _tok(rng, (2, P), H, d)
+    O, states = p.verify_direct(tok, slots)
+    np.testing.assert_array_equal(O, r.verify(tok, slots))
+    for n in range(2):
+        _, O_scan, snaps = kda_scan(S0[n], *(tok[x][n] for x in "qkvab"), snapshot_every=1)
+        np.testing.assert_allclose(O[n], O_scan, atol=1e-14)
+        for j in range(P):
+            np.testing.assert_allclose(states[n, j], snaps[j], atol=1e-14)
+    assert np.array_equal(p.state[slots], S0)                     # committed state untouched
+    assert np.array_equal(p.ring_k, np.zeros_like(p.ring_k))       # ring untouched
+
+
+def test_direct_commit_equals_ring_replay():
+    """Keeping the stored state of 1 + n positions == replaying them from the ring; the ring
+    pointer moves only in the ring scheme. Out-of-range acceptance clamps in both."""
+    rng = np.random.default_rng(22)
+    H, d, P = 2, 8, 6
+    p, r = KDAPool(3, H, d, d, 9), KDAPool(3, H, d, d, 9)
+    slots = [p.alloc(), p.alloc(), p.alloc()]
+    assert [r.alloc(), r.alloc(), r.alloc()] == slots
+    S0 = rng.standard_normal((3, H, d, d))
+    p.state[slots] = S0
+    r.state[slots] = S0
+    tok = _tok(rng, (3, P), H, d)
+    _, states = p.verify_direct(tok, slots)
+    r.verify(tok, slots)
+    n_acc = [2, 0, 9]                                             # 9 > P - 1: clamped to 5
+    p.commit_direct(slots, n_acc, states)
+    r.commit(slots, n_acc)
+    np.testing.assert_allclose(p.state[slots], r.state[slots], atol=1e-13)
+    assert p.error_bits & ERR_NACC_RANGE and r.error_bits & ERR_NACC_RANGE
+    assert list(p.pos[slots]) == list(r.pos[slots]) == [3, 1, 6]
+    assert list(p.pending[slots]) == [0, 0, 0]
+    assert list(p.ring_head[slots]) == [0, 0, 0] and list(r.ring_head[slots]) == [3, 1, 6]
+
+
+def test_direct_and_ring_commits_do_not_mix():
+    rng = np.random.default_rng(23)
+    p = KDAPool(2, 1, 4, 4, 9)
+    a, b = p.alloc(), p.alloc()
+    tok = _tok(rng, (1, 3), 1, 4)
+    _, states = p.verify_direct(tok, [a])
+    p.verify(tok, [b])
+    with pytest.raises(RuntimeError):
+        p.commit([a], [0])
+    with pytest.raises(RuntimeError):
+        p.commit_direct([b], [0], states)
+    before = p.state.copy()
+    p.rollback([a, b])                                            # either kind rolls back
+    assert np.array_equal(p.state, before) and list(p.pending) == [0, 0]
+    assert not p.direct.any()
+
+
 def test_checkpoint_equals_prefix_prefill():
     # The checkpoint exported after m*interval tokens equals the final state of a prefill
     # that stops at that boundary.
