@@ -4,4 +4,4 @@ The compute lives in the HIP library ``lib/libkda.so`` (C ABI in ``include/kda.h
 package is its Python binding. Importing it fails if the library has not been built.
 """
 from ._abi import KDAError, lib  # noqa: F401  (raises ImportError if libkda.so is missing)
-from .pool import IndexArray, KDAPool, chunk_for  # noqa: F401
+from .pool import IndexArray, KDAPool, chunk_for, prefix_hit  # noqa: F401

@@ -24,6 +24,21 @@ def chunk_for(d: int) -> int:
     return 16 if d == 16 else 64
 
 
+def prefix_hit(match_len: int, prompt_len: int, interval: int) -> int:
+    """Partial prefix-cache hit over KDA state checkpoints ("Kimi K3 is here: efficient day-0
+    support on vLLM", FAQ on prefix caching; "vLLM lifts Kimi K3 throughput by up to 2.8x",
+    section "KDA checkpoints stay inside the prefill"): a cached prompt left a state checkpoint
+    after every `interval` tokens, and a new prompt shares its first `match_len` tokens. The
+    state can resume from the deepest checkpoint inside the shared prefix, but at least one
+    prompt token is always prefilled so the step still produces the last prompt token's output.
+    Returns the number of prompt tokens the reused checkpoint covers (0: a miss); that
+    checkpoint is the (returned // interval - 1)-th of the cached prompt's."""
+    if interval <= 0 or prompt_len <= 0:
+        return 0
+    usable = min(max(match_len, 0), prompt_len - 1)
+    return usable // interval * interval
+
+
 def _stream(stream=None) -> c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return c_void_p(s.cuda_stream)

@@ -247,3 +247,14 @@ def test_mixed_batch_rejects_slot_overlap():
 def test_status_strings():
     for st in range(-6, 1):
         assert lib.kda_status_string(st)
+
+
+def test_prefix_hit_policy():
+    from recurrent_linear_attention_amd import prefix_hit
+    # (shared prefix, prompt length, checkpoint interval) -> tokens covered by the checkpoint
+    cases = [((0, 3000, 1024), 0), ((700, 3000, 1024), 0), ((1023, 3000, 1024), 0),
+             ((1024, 3000, 1024), 1024), ((2100, 3000, 1024), 2048), ((3000, 3000, 1024), 2048),
+             ((5000, 3000, 1024), 2048), ((2048, 2048, 1024), 1024), ((2049, 2049, 1024), 2048),
+             ((64, 65, 64), 64), ((64, 64, 64), 0), ((10, 10, 0), 0), ((-3, 10, 4), 0)]
+    for args, want in cases:
+        assert prefix_hit(*args) == want, (args, want)

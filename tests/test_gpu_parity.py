@@ -290,6 +290,51 @@ def test_prefill_ragged_with_resume_and_checkpoints(d):
     meta_equal(g.meta_array(), o.meta(), out + cks)
 
 
+def _cat(a: ki.Tokens, b: ki.Tokens) -> ki.Tokens:
+    t = ki.Tokens(*(torch.cat([getattr(a, n), getattr(b, n)]) for n in "qkvab"))
+    t.np = {n: np.concatenate([a.np[n], b.np[n]]) for n in a.np}
+    return t
+
+
+@pytest.mark.parametrize("match", [0, 700, 1024, 2100, 3000])
+def test_prefix_cache_hit_then_speculative_decode(match):
+    """Partial prefix-cache hit with speculative decode: a cached 3000-token prompt left state
+    checkpoints every 1024 tokens; a new prompt shares its first `match` tokens. The request
+    slot takes the deepest usable checkpoint (prefix_hit), prefills the rest of its prompt from
+    that offset in place, then verifies 1+4 drafts and commits 2. State, outputs and pos must
+    match the oracle running the whole new prompt from zero."""
+    H, d, I, L = 4, 128, 1024, 3000
+    g, o = pools(16, H, d)
+    rng = np.random.default_rng(70 + match)
+    cached = ki.draw_tokens(rng, (L,), H, d, d)
+    fresh = ki.draw_tokens(rng, (L,), H, d, d)
+    prompt = _cat(cached.slice(0, match), fresh.slice(match, L))
+    c_out, ck, req = 0, [1, 2], 5
+    g.kda_prefill(*tok_dev(cached), [0, L], [c_out], ckpt_slots=ck, ckpt_interval=I)
+    hit = kda.prefix_hit(match, L, I)
+    rest = prompt.slice(hit, L)
+    if hit:
+        g.kda_slot_checkpoint(ck[hit // I - 1], req)
+        O = g.kda_prefill(*tok_dev(rest), [0, L - hit], [req], init_slots=[req])
+    else:
+        O = g.kda_prefill(*tok_dev(rest), [0, L], [req])
+    drafts = ki.draw_tokens(rng, (1, 5), H, d, d)
+    Ov = g.kda_verify(*tok_dev(drafts), [req])
+    g.kda_commit([req], torch.tensor([2], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+    Oo = o.prefill(prompt.np, [0, L], [-1], [req], [], 0)
+    Ovo = o.verify(drafts.np, [req])
+    o.commit([req], [2])
+    assert rel_bf16(O, Oo[hit:]) <= TOL
+    assert rel_bf16(Ov, Ovo) <= TOL
+    assert rel(g.state[req], o.state[req]) <= TOL
+    m = g.meta_array()
+    assert int(m[req, 0]) == L + 3 and int(m[req, 2]) == 0
+    meta_equal(m, o.meta(), [req])
+    assert g.kda_read_device_error() == 0
+
+
 @pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 2), (32, 3), (32, 9)])
 def test_prefill_every_slice_width(H, n_seq):
     """sequences x heads of 28, 64 and 96 / 288 run the state pass with 16-, 32- and 64-column
