@@ -112,12 +112,14 @@ kda_status kda_slot_checkpoint(kda_pool* pool, int32_t src, int32_t dst, void* s
  * (floor(len_i / ckpt_interval) entries per sequence, concatenated in sequence order), each
  * with pos = init pos + boundary. All out and checkpoint slots must be live, idle and
  * distinct, and no init slot may be another sequence's out or checkpoint slot.
- * chunk must be the instantiated chunk for dk; ckpt_interval a multiple of chunk.
+ * chunk must be the instantiated chunk for dk. ckpt_interval may be any positive token
+ * count: every checkpoint position ends a chunk, so an interval that is not a multiple of
+ * the chunk cuts each interval into ceil(interval / chunk) chunks, the last one short.
  * Every h_* array is a host copy of the matching d_* device array (same contents); the host
  * copies drive validation, the device copies drive the kernels. Zero-length sequences are
  * allowed.
  * workspace: device memory, 256-byte aligned, of at least kda_prefill_workspace_bytes(pool,
- * n_tok, n_seq, chunk) bytes, owned by the caller and not touched by anything else until the
+ * n_tok, n_seq, chunk, ckpt_interval) bytes, owned by the caller and not touched by anything else until the
  * work on `stream` is done (the chunked form stages every chunk's S-independent operands there,
  * 65 KiB per chunk and head). NULL: the pool allocates its own buffer on first use and grows it
  * with hipMalloc (after a device synchronize) when a larger prefill comes; it is freed by
@@ -133,11 +135,12 @@ typedef struct {
   const int32_t* h_ckpt_slot;  const int32_t* d_ckpt_slot;    /* concat, or NULL        */
   void* workspace; size_t workspace_bytes;
 } kda_prefill_args;
-/* Workspace bytes that any prefill of n_tok tokens in n_seq sequences needs (an upper bound
- * over length mixes: at most floor(n_tok / chunk) + n_seq chunks); 0 where the token-by-token
- * kernel runs (dk = 16) or for n_seq <= 0.                                                 */
+/* Workspace bytes that any prefill of n_tok tokens in n_seq sequences with that checkpoint
+ * interval needs (an upper bound over length mixes: at most floor(n_tok / chunk) + n_seq
+ * chunks, plus floor(n_tok / ckpt_interval) when the interval is not a multiple of the
+ * chunk); 0 where the token-by-token kernel runs (dk = 16) or for n_seq <= 0.              */
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
-                                   int32_t chunk);
+                                   int32_t chunk, int32_t ckpt_interval);
 kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);
 
 /* ---- decode and speculative verify ---------------------------------------------------- */

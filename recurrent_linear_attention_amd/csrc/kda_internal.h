@@ -71,6 +71,30 @@ size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_ch
 // Token-by-token prefill with the decode step (reference-form kernel; any supported d).
 hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
 
+// Chunking of one sequence of len tokens with checkpoints every `interval` tokens (0: none).
+// Every checkpoint position ends a chunk ("vLLM lifts Kimi K3 throughput by up to 2.8x",
+// section "KDA checkpoints stay inside the prefill": the export happens inside the pass rather
+// than by splitting the prefill), so an interval that is not a multiple of the chunk splits
+// each interval into ceil(interval / chunk) chunks, the last one short; otherwise chunks are
+// chunk tokens from the sequence start and only the last one may be short.
+__host__ __device__ inline int seq_chunks(int len, int chunk, int interval) {
+  if (interval <= 0 || interval % chunk == 0) return (len + chunk - 1) / chunk;
+  const int per = (interval + chunk - 1) / chunk, full = len / interval, rem = len % interval;
+  return full * per + (rem + chunk - 1) / chunk;
+}
+// First token (relative to the sequence start) and token count of chunk c.
+__host__ __device__ inline void chunk_span(int c, int len, int chunk, int interval, int* t0, int* n) {
+  if (interval <= 0 || interval % chunk == 0) {
+    *t0 = chunk * c;
+    *n = len - *t0 < chunk ? len - *t0 : chunk;
+    return;
+  }
+  const int per = (interval + chunk - 1) / chunk, seg = c / per, j = c % per;
+  const int seg_len = len - seg * interval < interval ? len - seg * interval : interval;
+  *t0 = seg * interval + chunk * j;
+  *n = seg_len - chunk * j < chunk ? seg_len - chunk * j : chunk;
+}
+
 // Shapes the kernels are instantiated for.
 inline bool supported_dim(int d) { return d == 16 || d == 128; }
 inline int prefill_chunk_for(int d) { return d == 16 ? 16 : 64; }

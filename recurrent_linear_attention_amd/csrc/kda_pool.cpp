@@ -261,11 +261,13 @@ kda_status kda_slot_checkpoint(kda_pool* p, int32_t src, int32_t dst, void* stre
 }
 
 size_t kda_prefill_workspace_bytes(const kda_pool* p, int32_t n_tok, int32_t n_seq,
-                                   int32_t chunk) {
-  if (!p || n_tok < 0 || n_seq <= 0 || chunk <= 0) return 0;
-  // sum_i ceil(len_i / chunk) <= floor(n_tok / chunk) + n_seq
-  return kda::prefill_workspace_bytes(p->desc.dk, chunk, p->desc.num_heads, n_seq,
-                                      (int64_t)(n_tok / chunk) + n_seq);
+                                   int32_t chunk, int32_t ckpt_interval) {
+  if (!p || n_tok < 0 || n_seq <= 0 || chunk <= 0 || ckpt_interval < 0) return 0;
+  // sum_i seq_chunks(len_i) <= floor(n_tok / chunk) + n_seq, plus one more chunk per
+  // checkpoint boundary when the interval is not a multiple of the chunk
+  int64_t bound = (int64_t)(n_tok / chunk) + n_seq;
+  if (ckpt_interval > 0 && ckpt_interval % chunk != 0) bound += n_tok / ckpt_interval;
+  return kda::prefill_workspace_bytes(p->desc.dk, chunk, p->desc.num_heads, n_seq, bound);
 }
 
 static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool tensors_needed,
@@ -275,9 +277,8 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
   if (a->chunk != kda::prefill_chunk_for(p->desc.dk))
     return fail(KDA_EUNSUPPORTED, "chunk %d not instantiated for d=%d (use %d)", a->chunk,
                 p->desc.dk, kda::prefill_chunk_for(p->desc.dk));
-  if (a->ckpt_interval < 0 || (a->ckpt_interval > 0 && a->ckpt_interval % a->chunk != 0))
-    return fail(KDA_EUNSUPPORTED, "checkpoint interval %d must be a multiple of chunk %d",
-                a->ckpt_interval, a->chunk);
+  if (a->ckpt_interval < 0)
+    return fail(KDA_EUNSUPPORTED, "negative checkpoint interval %d", a->ckpt_interval);
   *n_chunks = 0;
   if (a->n_seq == 0) {
     *max_len = 0;
@@ -299,7 +300,7 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
     if (cu[i + 1] < cu[i]) return fail(KDA_EINVAL, "cu_seqlens must be non-decreasing");
     int32_t len = cu[i + 1] - cu[i];
     mx = len > mx ? len : mx;
-    nch += (len + a->chunk - 1) / a->chunk;
+    nch += kda::seq_chunks(len, a->chunk, a->ckpt_interval);
     if (a->ckpt_interval > 0) n_ckpt += len / a->ckpt_interval;
   }
   if (cu[a->n_seq] != a->n_tok) return fail(KDA_EINVAL, "cu_seqlens[n_seq] != n_tok");

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_
   int sc = 0, sk = 0;
   for (int j = j0; j < j1; ++j) {
     const int len = cu[j + 1] - cu[j];
-    sc += (len + PC - 1) / PC;
+    sc += seq_chunks(len, PC, ckpt_interval);
     sk += ckpt_interval > 0 ? len / ckpt_interval : 0;
   }
   // inclusive scan of the per-thread sums over the work-group (Hillis-Steele)
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_
     const int len = cu[j + 1] - cu[j];
     choff[j] = sc;
     ckoff[j] = sk;
-    sc += (len + PC - 1) / PC;
+    sc += seq_chunks(len, PC, ckpt_interval);
     sk += ckpt_interval > 0 ? len / ckpt_interval : 0;
   }
   if (n_seq > PLAN_MAX_SORT) {
@@ -237,8 +237,9 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
     if (choff[mid] <= gc) lo_i = mid; else hi_i = mid - 1;
   }
   const int si = lo_i, c = gc - choff[si];
-  const int tok0 = A.cu_seqlens[si] + PC * c;
-  const int n = min(PC, A.cu_seqlens[si + 1] - tok0);
+  int t0, n;
+  chunk_span(c, A.cu_seqlens[si + 1] - A.cu_seqlens[si], PC, A.ckpt_interval, &t0, &n);
+  const int tok0 = A.cu_seqlens[si] + t0;
   char* blk = blocks + (size_t)blockIdx.x * BLOCK_BYTES;
   const size_t hstride = (size_t)H * PD;
 
@@ -535,12 +536,14 @@ struct StateFetch {
   __device__ __forceinline__ StateFetch(const char* blk0, const PrefillLaunch& A, int c, int H, int lo,
                                         int len, int h, int col0, int t_, int w, uint32_t buf_)
       : bsrc(blk0 + (size_t)c * H * BLOCK_BYTES),
-        vsrc(A.t.v + (size_t)(lo + PC * c) * H * PD + (size_t)h * PD + col0),
         buf(buf_),
         wb((uint32_t)__builtin_amdgcn_readfirstlane((int)(buf_ + 16 * 64 * w))),
-        n(min(PC, len - PC * c)),
         hstr(H * PD),
-        t(t_) {}
+        t(t_) {
+    int t0;
+    chunk_span(c, len, PC, A.ckpt_interval, &t0, &n);
+    vsrc = A.t.v + (size_t)(lo + t0) * H * PD + (size_t)h * PD + col0;
+  }
   __device__ __forceinline__ void units(int off, int count) const {
 #pragma unroll
     for (int j = 0; j < count; ++j) lds_dma16(bsrc + off + 16 * (t + NT * j), wb + off + 16 * NT * j);
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
             l = t & 63, l16 = l & 15, lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
-  const int nch = (len + PC - 1) / PC;
+  const int nch = seq_chunks(len, PC, A.ckpt_interval);
   int ck = A.ckpt_interval > 0 ? ckoff[si] : 0;
   const int init = A.init_slot ? A.init_slot[si] : -1;
   const bool has_init = init >= 0 && init < P.num_slots;
@@ -688,8 +691,9 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   };
 
   for (int c = 0; c < nch; ++c) {
-    const int n = min(PC, len - PC * c);
-    const int tok0 = lo + PC * c;
+    int t0, n;
+    chunk_span(c, len, PC, A.ckpt_interval, &t0, &n);
+    const int tok0 = lo + t0;
     const char* buf = lds[c & 1];
     const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
     const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + BLOCK_BYTES);
@@ -832,7 +836,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
 #undef KDA_FENCE
 
     // ---- checkpoint export inside the pass -------------------------------------------------
-    const int done = PC * c + n;
+    const int done = t0 + n;
     if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
       // uniform index: a scalar load through the constant address space (no vector-memory
       // wait behind the chunk's in-flight loads)

@@ -143,10 +143,10 @@ class KDAPool:
                 _dev(v, torch.bfloat16, "v"), _dev(a, torch.float32, "a"),
                 _dev(b, torch.float32, "b"), _dev(o, torch.bfloat16, "o"))
 
-    def _workspace(self, n_tok: int, n_seq: int, chunk: int):
+    def _workspace(self, n_tok: int, n_seq: int, chunk: int, interval: int):
         """Device workspace for a prefill of this size from torch's allocator, kept and grown
         per pool (the library then allocates nothing). Returns (pointer, bytes)."""
-        need = lib.kda_prefill_workspace_bytes(self.handle, n_tok, n_seq, chunk)
+        need = lib.kda_prefill_workspace_bytes(self.handle, n_tok, n_seq, chunk, max(interval, 0))
         if need == 0:
             return None, 0
         if self._ws is None or self._ws.numel() < need:
@@ -159,7 +159,7 @@ class KDAPool:
         args.n_tok = n_tok
         args.chunk = chunk
         args.ckpt_interval = interval
-        args.workspace, args.workspace_bytes = self._workspace(n_tok, args.n_seq, chunk)
+        args.workspace, args.workspace_bytes = self._workspace(n_tok, args.n_seq, chunk, interval)
         args.h_cu_seqlens, args.d_cu_seqlens = cu.h, cu.d
         if init is not None:
             args.h_init_slot, args.d_init_slot = init.h, init.d

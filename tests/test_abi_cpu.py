@@ -191,7 +191,7 @@ def test_prefill_validation_errors():
     cu, out = i32(0, 40, 64), i32(s[0], s[1])
     # chunk not instantiated / interval not a multiple of the chunk
     assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, chunk=32)), None) == _abi.KDA_EUNSUPPORTED
-    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, interval=24)), None) == _abi.KDA_EUNSUPPORTED
+    assert lib.kda_prefill(p.h, byref(prefill_args(cu, out, interval=-16)), None) == _abi.KDA_EUNSUPPORTED
     # cu_seqlens must start at 0, not decrease, and end at n_tok
     assert lib.kda_prefill(p.h, byref(prefill_args(i32(1, 40, 64), out)), None) == _abi.KDA_EINVAL
     assert lib.kda_prefill(p.h, byref(prefill_args(i32(0, 40, 30), out)), None) == _abi.KDA_EINVAL
@@ -214,13 +214,18 @@ def test_prefill_workspace_size_and_checks():
     s = [p.alloc()[1] for _ in range(3)]
     p16 = HostPool(H=4, d=16)
     # the token-by-token shape takes no workspace, nor does an empty call
-    assert lib.kda_prefill_workspace_bytes(p16.h, 1000, 3, 16) == 0
-    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 0, 64) == 0
+    assert lib.kda_prefill_workspace_bytes(p16.h, 1000, 3, 16, 0) == 0
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 0, 64, 0) == 0
     # at most floor(1000 / 64) + 3 = 18 chunks, 61,952 bytes per (chunk, head), plus a small plan
-    need = lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64)
+    need = lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64, 0)
     assert 18 * 4 * 61952 <= need < 19 * 4 * 61952
-    assert lib.kda_prefill_workspace_bytes(p.h, 1064, 3, 64) > need
-    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 4, 64) > need
+    assert lib.kda_prefill_workspace_bytes(p.h, 1064, 3, 64, 0) > need
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 4, 64, 0) > need
+    # an interval that is a multiple of the chunk adds nothing; any other adds one chunk per
+    # boundary: 1000 // 100 = 10 more
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64, 128) == need
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64, 100) == need + 10 * 4 * 61952
+    assert lib.kda_prefill_workspace_bytes(p.h, 1000, 3, 64, -1) == 0
     # lengths 640 + 360 -> 10 + 6 chunks; a too-small or misaligned buffer fails validation
     cu, out = i32(0, 640, 1000), i32(s[0], s[1])
     a = prefill_args(cu, out, chunk=64)

@@ -296,20 +296,21 @@ def _cat(a: ki.Tokens, b: ki.Tokens) -> ki.Tokens:
     return t
 
 
-@pytest.mark.parametrize("match", [0, 700, 1024, 2100, 3000])
-def test_prefix_cache_hit_then_speculative_decode(match):
+@pytest.mark.parametrize("match,I", [(0, 1024), (700, 1024), (1024, 1024), (2100, 1024),
+                                     (3000, 1024), (2100, 1000)])
+def test_prefix_cache_hit_then_speculative_decode(match, I):
     """Partial prefix-cache hit with speculative decode: a cached 3000-token prompt left state
-    checkpoints every 1024 tokens; a new prompt shares its first `match` tokens. The request
+    checkpoints every I tokens; a new prompt shares its first `match` tokens. The request
     slot takes the deepest usable checkpoint (prefix_hit), prefills the rest of its prompt from
     that offset in place, then verifies 1+4 drafts and commits 2. State, outputs and pos must
     match the oracle running the whole new prompt from zero."""
-    H, d, I, L = 4, 128, 1024, 3000
+    H, d, L = 4, 128, 3000
     g, o = pools(16, H, d)
-    rng = np.random.default_rng(70 + match)
+    rng = np.random.default_rng(70 + match + I)
     cached = ki.draw_tokens(rng, (L,), H, d, d)
     fresh = ki.draw_tokens(rng, (L,), H, d, d)
     prompt = _cat(cached.slice(0, match), fresh.slice(match, L))
-    c_out, ck, req = 0, [1, 2], 5
+    c_out, ck, req = 0, list(range(1, 1 + L // I)), 10
     g.kda_prefill(*tok_dev(cached), [0, L], [c_out], ckpt_slots=ck, ckpt_interval=I)
     hit = kda.prefix_hit(match, L, I)
     rest = prompt.slice(hit, L)
@@ -332,6 +333,35 @@ def test_prefix_cache_hit_then_speculative_decode(match):
     m = g.meta_array()
     assert int(m[req, 0]) == L + 3 and int(m[req, 2]) == 0
     meta_equal(m, o.meta(), [req])
+    assert g.kda_read_device_error() == 0
+
+
+@pytest.mark.parametrize("d,interval", [(128, 100), (128, 37), (128, 65), (128, 1000), (16, 10), (16, 24)])
+def test_prefill_checkpoints_at_unaligned_intervals(d, interval):
+    """Checkpoint intervals that are not a multiple of the chunk: every boundary ends a chunk
+    inside the pass (short chunks mid-sequence). Ragged lengths, resumed sequences, all
+    checkpoints and outputs against the oracle."""
+    H = 4
+    lengths = [0, 1, interval - 1, interval, interval + 1, 3 * interval + 7, 7 * interval + 3, 64]
+    n = len(lengths)
+    g, o = pools(64, H, d)
+    rng = np.random.default_rng(80 + d + interval)
+    init = [-1, 40, -1, 41, -1, 42, -1, 43]
+    put_states(g, o, [40, 41, 42, 43], ki.draw_states(rng, 4, H, d, d))
+    out = [0, 1, 2, 41, 4, 5, 6, 7]          # sequence 3 updates its init slot in place
+    n_ck = sum(L // interval for L in lengths)
+    cks = list(range(8, 8 + n_ck))
+    assert 8 + n_ck <= 40
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks,
+                      ckpt_interval=interval)
+    Oo = o.prefill(tok.np, cu, init, out, cks, interval)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    for s_ in out + cks:
+        assert rel(g.state[s_], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), out + cks)
     assert g.kda_read_device_error() == 0
 
 
