@@ -210,8 +210,8 @@ kda_status kda_commit_direct(kda_pool* pool, int32_t B, const int32_t* h_slots,
  * n_decode decode tokens follow, then n_verify * n_pos verify tokens ([seq][pos] order).
  * o is written in the same packing, with no gather or scatter; the prefill's token pointers
  * and the step slot arrays of `prefill`, `decode` and `verify` are ignored in favour of the
- * packed ones below. Decode and verify touch only their own slots, so when the batch also
- * has a prefill they run on a side stream owned by the pool (default priority, created on
+ * packed ones below. Commit, decode and verify touch only their own slots, so when the batch
+ * also has a prefill they run (in that order) on a side stream owned by the pool (default priority, created on
  * first use, destroyed by kda_pool_destroy) while the prefill's sequential pass runs on
  * `stream`: forked by an event recorded on `stream` after the prefill's first kernels,
  * joined by an event that `stream` waits on before the call returns. Everything enqueued on
@@ -225,6 +225,12 @@ typedef struct {
   const int32_t* h_decode_slots; const int32_t* d_decode_slots;
   int32_t n_verify, n_pos;
   const int32_t* h_verify_slots; const int32_t* d_verify_slots;
+  /* ReplaySSM commits of slots pending from an earlier verify (typically the previous
+   * step's), as kda_commit with d_n_accepted: they run before this batch's decode and verify,
+   * which may name the same slots again; they must not be any prefill slot. 0 = none.   */
+  int32_t n_commit;
+  const int32_t* h_commit_slots; const int32_t* d_commit_slots;
+  const int32_t* d_n_accepted;
 } kda_mixed_args;
 kda_status kda_mixed_batch(kda_pool* pool, const kda_mixed_args* args, void* stream);
 

@@ -56,7 +56,9 @@ class kda_mixed_args(ctypes.Structure):
                 ("b", c_void_p), ("o", c_void_p), ("prefill", kda_prefill_args),
                 ("n_decode", c_int32), ("h_decode_slots", c_void_p),
                 ("d_decode_slots", c_void_p), ("n_verify", c_int32), ("n_pos", c_int32),
-                ("h_verify_slots", c_void_p), ("d_verify_slots", c_void_p)]
+                ("h_verify_slots", c_void_p), ("d_verify_slots", c_void_p),
+                ("n_commit", c_int32), ("h_commit_slots", c_void_p), ("d_commit_slots", c_void_p),
+                ("d_n_accepted", c_void_p)]
 
 
 # name -> (restype, argtypes); every symbol include/kda.h declares.

@@ -440,7 +440,7 @@ kda_status kda_rollback(kda_pool* p, int32_t B, const int32_t* h_slots, const in
 kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   if (!p || !m) return fail(KDA_EINVAL, "null argument");
   const int32_t H = p->desc.num_heads, dk = p->desc.dk, dv = p->desc.dv;
-  if (m->n_decode < 0 || m->n_verify < 0) return fail(KDA_EINVAL, "negative batch");
+  if (m->n_decode < 0 || m->n_verify < 0 || m->n_commit < 0) return fail(KDA_EINVAL, "negative batch");
   if (m->n_verify > 0 && (m->n_pos < 1 || m->n_pos > p->desc.ring_cap))
     return fail(KDA_EINVAL, "n_pos %d outside 1..ring_cap", m->n_pos);
   kda_status st = check_tensors(m->q, m->k, m->v, m->a, m->b, m->o);
@@ -452,22 +452,36 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   int64_t n_chunks = 0;
   st = validate_prefill(p, &pre, false, &max_len, &n_chunks);
   if (st != KDA_OK) return st;
-  // Decode and verify slots: idle, distinct from each other and from the prefill's slots.
-  p->begin_pass();
-  for (int32_t i = 0; i < pre.n_seq; ++i) p->mark(pre.h_out_slot[i]);
-  if (pre.ckpt_interval > 0 && pre.h_ckpt_slot) {
-    int64_t n_ckpt = 0;
-    for (int32_t i = 0; i < pre.n_seq; ++i)
-      n_ckpt += (pre.h_cu_seqlens[i + 1] - pre.h_cu_seqlens[i]) / pre.ckpt_interval;
-    for (int64_t i = 0; i < n_ckpt; ++i) p->mark(pre.h_ckpt_slot[i]);
-  }
-  if (pre.h_init_slot)
-    for (int32_t i = 0; i < pre.n_seq; ++i)
-      if (pre.h_init_slot[i] >= 0) p->mark(pre.h_init_slot[i]);
+  auto mark_prefill_slots = [&]() {
+    p->begin_pass();
+    for (int32_t i = 0; i < pre.n_seq; ++i) p->mark(pre.h_out_slot[i]);
+    if (pre.ckpt_interval > 0 && pre.h_ckpt_slot) {
+      int64_t n_ckpt = 0;
+      for (int32_t i = 0; i < pre.n_seq; ++i)
+        n_ckpt += (pre.h_cu_seqlens[i + 1] - pre.h_cu_seqlens[i]) / pre.ckpt_interval;
+      for (int64_t i = 0; i < n_ckpt; ++i) p->mark(pre.h_ckpt_slot[i]);
+    }
+    if (pre.h_init_slot)
+      for (int32_t i = 0; i < pre.n_seq; ++i)
+        if (pre.h_init_slot[i] >= 0) p->mark(pre.h_init_slot[i]);
+  };
+  // Commit slots: pending a ring commit, distinct from each other and from the prefill's slots
+  // (the prefill is not ordered against the side stream).
+  mark_prefill_slots();
+  st = check_slots(p, m->n_commit, m->h_commit_slots, SLOT_PENDING, false);
+  if (st != KDA_OK) return st;
+  if (m->n_commit > 0 && (!m->d_commit_slots || !m->d_n_accepted))
+    return fail(KDA_EINVAL, "null device commit array");
+  // Decode and verify slots: idle once the commits are done (they run first, in order on the
+  // same stream), distinct from each other and from the prefill's slots.
+  for (int32_t i = 0; i < m->n_commit; ++i) p->slot_state[m->h_commit_slots[i]] = SLOT_IDLE;
+  mark_prefill_slots();
   st = check_slots(p, m->n_decode, m->h_decode_slots, SLOT_IDLE, false);
-  if (st != KDA_OK) return st;
-  st = check_slots(p, m->n_verify, m->h_verify_slots, SLOT_IDLE, false);
-  if (st != KDA_OK) return st;
+  if (st == KDA_OK) st = check_slots(p, m->n_verify, m->h_verify_slots, SLOT_IDLE, false);
+  if (st != KDA_OK) {
+    for (int32_t i = 0; i < m->n_commit; ++i) p->slot_state[m->h_commit_slots[i]] = SLOT_PENDING;
+    return st;
+  }
   if ((m->n_decode > 0 && !m->d_decode_slots) || (m->n_verify > 0 && !m->d_verify_slots))
     return fail(KDA_EINVAL, "null device slot array");
 
@@ -479,10 +493,10 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
                    static_cast<const uint16_t*>(m->v) + row * H * dv, m->a + row * H * dk,
                    m->b + row * H, static_cast<uint16_t*>(m->o) + row * H * dv);
   };
-  // Decode and verify touch only their own slots (checked distinct above), so they need no
-  // order against the prefill: with a prefill in the batch they go to the side stream once
-  // the prefill's S-independent kernel is enqueued, and the caller's stream waits for them
-  // before anything later.
+  // Commit, decode and verify touch only their own slots (checked distinct from the
+  // prefill's above), so they need no order against the prefill: with a prefill in the batch
+  // they go to the side stream, in that order, once the prefill's S-independent kernel is
+  // enqueued, and the caller's stream waits for them before anything later.
   struct StepLaunches {
     kda_pool* p;
     const kda_mixed_args* m;
@@ -491,6 +505,10 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     bool fork;
     hipError_t run(hipStream_t on) const {
       hipError_t e = hipSuccess;
+      if (m->n_commit > 0) {
+        e = kda::launch_commit(p->view, m->n_commit, m->d_commit_slots, m->d_n_accepted, on);
+        if (e != hipSuccess) return e;
+      }
       if (m->n_decode > 0) {
         e = kda::launch_decode(p->view, dec, m->n_decode, m->d_decode_slots, on);
         if (e != hipSuccess) return e;
@@ -508,7 +526,7 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
       return e;
     }
   };
-  const bool steps = m->n_decode > 0 || m->n_verify > 0;
+  const bool steps = m->n_decode > 0 || m->n_verify > 0 || m->n_commit > 0;
   StepLaunches sl{p, m, part(n_pre), part(n_pre + m->n_decode), s, pre.n_seq > 0 && steps};
   hipError_t e = hipSuccess;
   if (sl.fork && !p->aux) {
@@ -533,7 +551,7 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     }
   } else if (steps) {
     e = sl.run(s);
-    if (e != hipSuccess) return hip_fail(e, "mixed: decode / verify launch");
+    if (e != hipSuccess) return hip_fail(e, "mixed: commit / decode / verify launch");
   }
   for (int32_t i = 0; i < m->n_verify; ++i) p->slot_state[m->h_verify_slots[i]] = SLOT_PENDING;
   return KDA_OK;

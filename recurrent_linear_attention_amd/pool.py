@@ -258,8 +258,11 @@ class KDAPool:
 
     def kda_mixed_batch(self, q, k, v, a, b, cu_seqlens, out_slots, decode_slots,
                         verify_slots, n_pos: int, init_slots=None, ckpt_slots=None,
-                        ckpt_interval: int = 0, o=None, stream=None) -> torch.Tensor:
-        """One packed batch [prefill tokens | decode tokens | verify tokens ([seq][pos])]."""
+                        ckpt_interval: int = 0, o=None, stream=None, commit_slots=None,
+                        n_accepted: torch.Tensor | None = None) -> torch.Tensor:
+        """One packed batch [prefill tokens | decode tokens | verify tokens ([seq][pos])].
+        commit_slots / n_accepted (device int32): ReplaySSM commits of slots pending from an
+        earlier verify, run before this batch's decode and verify."""
         if o is None:
             o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
         ptrs = self._tok_ptrs(q, k, v, a, b, o)
@@ -275,6 +278,10 @@ class KDAPool:
         m.n_decode, m.h_decode_slots, m.d_decode_slots = dec.np.size, dec.h, dec.d
         m.n_verify, m.n_pos = ver.np.size, n_pos
         m.h_verify_slots, m.d_verify_slots = ver.h, ver.d
+        if commit_slots is not None:
+            com = _ix(commit_slots, self.device)
+            m.n_commit, m.h_commit_slots, m.d_commit_slots = com.np.size, com.h, com.d
+            m.d_n_accepted = _dev(n_accepted, torch.int32, "n_accepted")
         check(lib.kda_mixed_batch(self.handle, byref(m), _stream(stream)), "kda_mixed_batch")
         return o
 

@@ -249,6 +249,25 @@ def test_mixed_batch_rejects_slot_overlap():
     assert lib.kda_slot_host_state(p.h, s[2]) == 1      # verify slot not marked pending
 
 
+def test_mixed_batch_commit_part_validation():
+    p = HostPool()
+    s = [p.alloc()[1] for _ in range(4)]
+    m = _abi.kda_mixed_args(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cu, out = i32(0, 32), i32(s[0])
+    m.prefill = prefill_args(cu, out)
+    com = i32(s[1])
+    m.n_commit, m.h_commit_slots, m.d_commit_slots, m.d_n_accepted = 1, com.ctypes.data, FAKE, FAKE
+    # committing an idle slot: wrong state, nothing changes
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_ESTATE
+    assert lib.kda_slot_host_state(p.h, s[1]) == 1
+    # a commit slot may not be a prefill slot
+    com2 = i32(s[0])
+    m.h_commit_slots = com2.ctypes.data
+    assert lib.kda_mixed_batch(p.h, byref(m), None) in (_abi.KDA_EINVAL, _abi.KDA_ESTATE)
+    m.n_commit = -1
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+
+
 def test_status_strings():
     for st in range(-6, 1):
         assert lib.kda_status_string(st)

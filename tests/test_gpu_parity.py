@@ -596,6 +596,46 @@ def test_mixed_batch_full_size_sampled():
     assert g.kda_read_device_error() == 0
 
 
+def test_mixed_batch_commits_previous_verify():
+    """Two serving steps: the second mixed batch commits the first one's verified drafts (its
+    commit part) before verifying the same slots again, next to a new prefill and decodes.
+    Every output, state and metadata entry against the oracle applying the same operations in
+    order."""
+    H, d, P = 4, 128, 5
+    g, o = pools(32, H, d)
+    rng = np.random.default_rng(90)
+    ds, vs = np.array([3, 7, 11], np.int32), np.array([5, 20], np.int32)
+    put_states(g, o, np.concatenate([ds, vs]), ki.draw_states(rng, 5, H, d, d))
+
+    def step(pre_len, out, commit, n_acc):
+        cu = np.concatenate([[0], np.cumsum(pre_len)]).astype(np.int32)
+        n_pre = int(cu[-1])
+        tok = ki.draw_tokens(rng, (n_pre + len(ds) + len(vs) * P,), H, d, d)
+        kw = {}
+        if commit is not None:
+            kw = dict(commit_slots=commit, n_accepted=torch.tensor(n_acc, dtype=torch.int32, device="cuda"))
+            o.commit(commit, n_acc)
+        O = g.kda_mixed_batch(*tok_dev(tok), cu, out, ds, vs, P, **kw)
+        Op = o.prefill(tok.slice(0, n_pre).np, cu, [-1] * len(out), out, [], 0)
+        Od = o.decode(tok.slice(n_pre, n_pre + len(ds)).np, ds)
+        vt = {n: x[n_pre + len(ds):].reshape((len(vs), P) + x.shape[1:]) for n, x in tok.np.items()}
+        Ov = o.verify(vt, vs)
+        torch.cuda.synchronize()
+        assert rel_bf16(O[:n_pre], Op) <= TOL
+        assert rel_bf16(O[n_pre:n_pre + len(ds)], Od) <= TOL
+        assert rel_bf16(O[n_pre + len(ds):].reshape(len(vs), P, H, d), Ov) <= TOL
+
+    step([300, 100], [0, 1], None, None)
+    step([200, 257], [2, 4], vs, [3, 0])
+    touched = [0, 1, 2, 4] + ds.tolist() + vs.tolist()
+    for s_ in touched:
+        assert rel(g.state[s_], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), touched)
+    ring_check(g, o, vs)
+    assert all(g.host_state(int(s_)) == 2 for s_ in vs)
+    assert g.kda_read_device_error() == 0
+
+
 # ----------------------------------------------------------------------------- slot ops
 
 def test_slot_reset_and_checkpoint_copy():
