@@ -47,10 +47,10 @@ RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
 # bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid only for the kernel source it was
 # measured on (first 16 hex digits of its SHA-256); for any other source the bench reports
 # traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "e6ad82aeba0c27e6", "fetch_scale": 2.0, "write_scale": 1.0,
-                   "fetch_kib": {"prefill_plan_kernel": 4, "chunk_prep_kernel": 269321,
-                                 "state_pass_kernel<4, 1, 4>": 316060},
-                   "write_kib": {"prefill_plan_kernel": 0, "chunk_prep_kernel": 501673,
+PREFILL_TRAFFIC = {"source_sha256_16": "12fa5babe31142fb", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"prefill_plan_kernel": 5, "chunk_prep_kernel": 269324,
+                                 "state_pass_kernel<4, 1, 4>": 316062},
+                   "write_kib": {"prefill_plan_kernel": 0, "chunk_prep_kernel": 501746,
                                  "state_pass_kernel<4, 1, 4>": 142818}}
 
 
