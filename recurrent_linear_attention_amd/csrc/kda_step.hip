@@ -128,22 +128,48 @@ __device__ __forceinline__ void step(float (&S)[C::RPT][4], const StepIn<C>& in,
   }
 }
 
-// Inputs of one position: k, a (and q) rows r0..r0+RPT-1 and v columns c0..c0+3.
+// Raw inputs of one position as loaded: k, a (and q) rows r0..r0+RPT-1 and v columns
+// c0..c0+3. Loops over positions fetch position j + 1 while position j is stepped, so only
+// the first position's load latency is exposed.
+template <class C>
+struct StepRaw {
+  uint32_t kw[(C::RPT + 1) / 2], qw[(C::RPT + 1) / 2], vw[2];
+  float a[C::RPT];
+  float b;
+};
+
+template <class C, bool WITH_Q>
+__device__ __forceinline__ void fetch_in(StepRaw<C>& r, const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* v, const float* a, const float* b,
+                                         int r0, int c0) {
+  load_bf16_raw<C::RPT>(k + r0, r.kw);
+  if constexpr (WITH_Q) load_bf16_raw<C::RPT>(q + r0, r.qw);
+  load_f32<C::RPT>(a + r0, r.a);
+  load_bf16_raw<4>(v + c0, r.vw);
+  r.b = *b;
+}
+
+template <class C, bool WITH_Q>
+__device__ __forceinline__ void unpack_in(StepIn<C>& in, const StepRaw<C>& r) {
+#pragma unroll
+  for (int i = 0; i < (C::RPT + 1) / 2; ++i) in.kw[i] = r.kw[i];
+  unpack_bf16<C::RPT>(r.kw, in.k);
+  if constexpr (WITH_Q) unpack_bf16<C::RPT>(r.qw, in.q);
+#pragma unroll
+  for (int i = 0; i < C::RPT; ++i) in.a[i] = r.a[i];
+  in.vw[0] = r.vw[0];
+  in.vw[1] = r.vw[1];
+  unpack_bf16<4>(r.vw, in.v);
+  in.b = r.b;
+}
+
 template <class C, bool WITH_Q>
 __device__ __forceinline__ void load_in(StepIn<C>& in, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* v, const float* a, const float* b,
                                         int r0, int c0) {
-  load_bf16_raw<C::RPT>(k + r0, in.kw);
-  unpack_bf16<C::RPT>(in.kw, in.k);
-  if constexpr (WITH_Q) {
-    uint32_t qw[(C::RPT + 1) / 2];
-    load_bf16_raw<C::RPT>(q + r0, qw);
-    unpack_bf16<C::RPT>(qw, in.q);
-  }
-  load_f32<C::RPT>(a + r0, in.a);
-  load_bf16_raw<4>(v + c0, in.vw);
-  unpack_bf16<4>(in.vw, in.v);
-  in.b = *b;
+  StepRaw<C> r;
+  fetch_in<C, WITH_Q>(r, q, k, v, a, b, r0, c0);
+  unpack_in<C, WITH_Q>(in, r);
 }
 
 template <class C>
@@ -164,6 +190,17 @@ __device__ __forceinline__ void store_state(const float (&S)[C::RPT][4], float* 
 }
 
 __device__ __forceinline__ int wrap(int x, int R) { return ((x % R) + R) % R; }
+
+// An empty use of every state register: the compiler places the wait for the state loads here,
+// before a loop over positions, instead of at their first use inside the loop, where it would
+// also wait for the next position's prefetched inputs on every iteration.
+template <class C>
+__device__ __forceinline__ void state_ready(const float (&S)[C::RPT][4]) {
+#pragma unroll
+  for (int r = 0; r < C::RPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(S[r][c]));
+}
 
 // grid: B * H * (D / VS); block (bi, h, vs) with vs fastest.
 template <int D>
@@ -216,10 +253,18 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
   const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
   float S[C::RPT][4];
   load_state<C>(S, Sp, r0, c0);
+  auto fetch = [&](StepRaw<C>& r, int j) {
+    const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
+    fetch_in<C, true>(r, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+  };
+  StepRaw<C> nxt;
+  fetch(nxt, 0);
+  state_ready<C>(S);
   for (int j = 0; j < n_pos; ++j) {
     const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
     StepIn<C> in;
-    load_in<C, true>(in, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+    unpack_in<C, true>(in, nxt);
+    if (j + 1 < n_pos) fetch(nxt, j + 1);
     float o[4];
     step<C, true>(S, in, lds, j & 1, o);
     const size_t e = ((size_t)slot * R + (size_t)wrap(head + j, R)) * P.H + h;
@@ -267,11 +312,18 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, cons
   float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
   float S[C::RPT][4];
   load_state<C>(S, Sp, r0, c0);
-  for (int j = 0; j < n; ++j) {
+  auto fetch = [&](StepRaw<C>& r, int j) {
     const size_t e = ((size_t)slot * R + (size_t)wrap(vb + j, R)) * P.H + h;
+    fetch_in<C, false>(r, nullptr, P.ring_k + e * D, P.ring_v + e * D, P.ring_a + e * D, P.ring_b + e,
+                       r0, c0);
+  };
+  StepRaw<C> nxt;
+  fetch(nxt, 0);
+  state_ready<C>(S);
+  for (int j = 0; j < n; ++j) {
     StepIn<C> in;
-    load_in<C, false>(in, nullptr, P.ring_k + e * D, P.ring_v + e * D, P.ring_a + e * D,
-                      P.ring_b + e, r0, c0);
+    unpack_in<C, false>(in, nxt);
+    if (j + 1 < n) fetch(nxt, j + 1);
     float o[4];
     step<C, false>(S, in, lds, j & 1, o);
   }
@@ -307,10 +359,18 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_direct_kernel(PoolView 
   const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
   float S[C::RPT][4];
   load_state<C>(S, Sp, r0, c0);
+  auto fetch = [&](StepRaw<C>& r, int j) {
+    const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
+    fetch_in<C, true>(r, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+  };
+  StepRaw<C> nxt;
+  fetch(nxt, 0);
+  state_ready<C>(S);
   for (int j = 0; j < n_pos; ++j) {
     const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
     StepIn<C> in;
-    load_in<C, true>(in, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
+    unpack_in<C, true>(in, nxt);
+    if (j + 1 < n_pos) fetch(nxt, j + 1);
     float o[4];
     step<C, true>(S, in, lds, j & 1, o);
     if (rg == 0) {
@@ -386,11 +446,19 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void prefill_recurrent_kernel(PoolV
       for (int c = 0; c < 4; ++c) S[r][c] = 0.f;
   }
   const int64_t pos0 = (init >= 0 && init < P.num_slots) ? P.meta[init].pos : 0;
+  auto fetch = [&](StepRaw<C>& r, int tok) {
+    const size_t row = (size_t)tok * P.H + h;
+    fetch_in<C, true>(r, A.t.q + row * D, A.t.k + row * D, A.t.v + row * D, A.t.a + row * D,
+                      A.t.b + row, r0, c0);
+  };
+  StepRaw<C> nxt;
+  if (lo < hi) fetch(nxt, lo);
+  state_ready<C>(S);
   for (int tok = lo; tok < hi; ++tok) {
     const size_t row = (size_t)tok * P.H + h;
     StepIn<C> in;
-    load_in<C, true>(in, A.t.q + row * D, A.t.k + row * D, A.t.v + row * D, A.t.a + row * D,
-                     A.t.b + row, r0, c0);
+    unpack_in<C, true>(in, nxt);
+    if (tok + 1 < hi) fetch(nxt, tok + 1);
     float o[4];
     step<C, true>(S, in, lds, tok & 1, o);
     if (rg == 0) {
