@@ -166,6 +166,33 @@ __global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_
   }
 }
 
+// A batch of at most 64 sequences is planned inside chunk_prep_kernel instead (one lane per
+// sequence), which saves the plan kernel's launch: lane i gets sequence i's length, chunk count
+// and exclusive chunk / checkpoint offsets.
+constexpr int PLAN_INLINE_MAX = 64;
+struct LanePlan {
+  int len, nch, choff, ckoff, n_ck;
+};
+__device__ __forceinline__ LanePlan lane_plan(const int32_t* cu, int n_seq, int interval, int lane) {
+  LanePlan q{0, 0, 0, 0, 0};
+  if (lane < n_seq) {
+    q.len = cu[lane + 1] - cu[lane];
+    q.nch = seq_chunks(q.len, PC, interval);
+    q.n_ck = interval > 0 ? q.len / interval : 0;
+  }
+  int c = q.nch, k = q.n_ck;   // inclusive scans over the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const int cc = __shfl_up(c, off), kk = __shfl_up(k, off);
+    if (lane >= off) {
+      c += cc;
+      k += kk;
+    }
+  }
+  q.choff = c - q.nch;
+  q.ckoff = k - q.n_ck;
+  return q;
+}
+
 // ---- chunk_prep_kernel: the S-independent part of one (chunk, head) -------------------------
 constexpr int PNW = 8;            // waves per work-group
 constexpr int PNT = 64 * PNW;
@@ -224,19 +251,45 @@ __device__ __forceinline__ void t_column(const PrepLds& L, char* blk, int l16, i
 
 // One work-group per (chunk, head): blockIdx.x = global chunk index * H + head. Thread t
 // owns key rows 4m .. 4m+3 (m = t / 32) and key channels 4cq .. 4cq+3 (cq = t % 32) in the
-// staging and operand phases.
+// staging and operand phases. For batches of at most PLAN_INLINE_MAX sequences every wave plans
+// the batch itself and work-group 0 writes the plan arrays for the state pass; larger batches
+// read choff from the plan kernel.
 __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillLaunch A,
-                                                            const int32_t* __restrict__ choff,
+                                                            int32_t* __restrict__ choff,
+                                                            int32_t* __restrict__ ckoff,
+                                                            int32_t* __restrict__ order,
                                                             char* __restrict__ blocks) {
   __shared__ PrepLds L;
   const int H = P.H, h = blockIdx.x % H, gc = blockIdx.x / H;
-  // sequence of this chunk: the last i with choff[i] <= gc (binary search, uniform)
-  int lo_i = 0, hi_i = A.n_seq - 1;
-  while (lo_i < hi_i) {
-    const int mid = (lo_i + hi_i + 1) >> 1;
-    if (choff[mid] <= gc) lo_i = mid; else hi_i = mid - 1;
+  int si, c;
+  if (A.n_seq <= PLAN_INLINE_MAX) {
+    const int lane = (int)threadIdx.x & 63;
+    const LanePlan q = lane_plan(A.cu_seqlens, A.n_seq, A.ckpt_interval, lane);
+    // the sequence whose chunk range holds gc (every chunk of the grid lies in one)
+    const uint64_t hit = __ballot(lane < A.n_seq && q.choff <= gc && gc < q.choff + q.nch);
+    si = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+    c = gc - __shfl(q.choff, si);
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < A.n_seq) {
+      choff[lane] = q.choff;
+      ckoff[lane] = q.ckoff;
+      if (lane == A.n_seq - 1) choff[A.n_seq] = q.choff + q.nch;
+      int rank = 0;   // descending length, ties: lower index first
+      for (int k = 0; k < A.n_seq; ++k) {
+        const int lk = __shfl(q.len, k);
+        rank += (lk > q.len) || (lk == q.len && k < lane);
+      }
+      order[rank] = lane;
+    }
+  } else {
+    // the last i with choff[i] <= gc (binary search, uniform)
+    int lo_i = 0, hi_i = A.n_seq - 1;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i + 1) >> 1;
+      if (choff[mid] <= gc) lo_i = mid; else hi_i = mid - 1;
+    }
+    si = lo_i;
+    c = gc - choff[si];
   }
-  const int si = lo_i, c = gc - choff[si];
   int t0, n;
   chunk_span(c, A.cu_seqlens[si + 1] - A.cu_seqlens[si], PC, A.ckpt_interval, &t0, &n);
   const int tok0 = A.cu_seqlens[si] + t0;
@@ -916,13 +969,16 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
   int32_t* ckoff = choff + (a.n_seq + 1);
   int32_t* order = ckoff + a.n_seq;
   char* blocks = ws + plan_bytes(a.n_seq);
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a.cu_seqlens, a.n_seq,
-                     a.ckpt_interval, choff, ckoff, order);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (a.n_seq > PLAN_INLINE_MAX || a.n_chunks == 0) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a.cu_seqlens, a.n_seq,
+                       a.ckpt_interval, choff, ckoff, order);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.n_chunks > 0) {
     hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(a.n_chunks * p.H)), dim3(PNT), 0, s, p, a,
-                       choff, blocks);
+                       choff, ckoff, order, blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

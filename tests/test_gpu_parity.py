@@ -474,6 +474,55 @@ def test_prefill_many_short_sequences(n_seq, H):
     assert g.kda_read_device_error() == 0
 
 
+
+@pytest.mark.parametrize("n_seq", [63, 64, 65])
+def test_prefill_plan_inside_and_outside_the_operand_kernel(n_seq):
+    """Up to 64 sequences the operand kernel plans the batch itself (one lane per sequence);
+    from 65 on the plan kernel does. Both sides of the boundary, with resumed sequences,
+    checkpoints every 128 tokens, ties in length and empty sequences: outputs, final and
+    checkpoint states against the oracle, checkpoint metadata exact."""
+    rng = np.random.default_rng(900 + n_seq)
+    H, d, interval = 2, 128, 128
+    lengths = [int(x) for x in rng.choice([0, 5, 64, 130, 300, 700], size=n_seq)]
+    lengths[0], lengths[1] = 700, 700    # a tie for the longest
+    n_ck = sum(L // interval for L in lengths)
+    n_slots = 2 * n_seq + n_ck
+    g, o = pools(n_slots, H, d)
+    init = [i if i % 3 == 0 else -1 for i in range(n_seq)]
+    states = ki.draw_states(rng, n_seq, H, d, d)
+    put_states(g, o, range(n_seq), states)
+    out = list(range(n_seq, 2 * n_seq))
+    cks = list(range(2 * n_seq, n_slots))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks,
+                      ckpt_interval=interval)
+    torch.cuda.synchronize()
+    Oo = o.prefill(tok.np, cu, init, out, cks, interval)
+    assert rel_bf16(O, Oo) <= TOL
+    for s_ in out + cks:
+        assert rel(g.state[s_], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), out + cks)
+    assert g.kda_read_device_error() == 0
+
+
+def test_prefill_only_empty_sequences():
+    """A batch whose sequences are all empty has no chunk: the plan kernel runs, no operand
+    kernel, and the state pass copies each init state (or zero) to its out slot."""
+    rng = np.random.default_rng(77)
+    H, d = 4, 128
+    g, o = pools(8, H, d)
+    put_states(g, o, [0, 1], ki.draw_states(rng, 2, H, d, d))
+    cu = np.zeros(4, np.int32)
+    tok = ki.draw_tokens(rng, (0,), H, d, d)
+    g.kda_prefill(*tok_dev(tok), cu, [4, 5, 6], init_slots=[0, -1, 1])
+    torch.cuda.synchronize()
+    o.prefill(tok.np, cu, [0, -1, 1], [4, 5, 6], [], 0)
+    for s_ in (4, 5, 6):
+        np.testing.assert_array_equal(f64(g.state[s_]), o.state[s_])
+    meta_equal(g.meta_array(), o.meta(), [4, 5, 6])
+    assert g.kda_read_device_error() == 0
+
 def test_prefill_one_long_and_five_short():
     """One long prompt (not first in the batch) and five short ones at 32 heads: the long one
     starts first and the short ones share the remaining CUs. Checkpoints, a resumed short
