@@ -8,7 +8,7 @@ kda_mixed_batch call -- on H=32 heads
 seeded (kda_inputs.mixed_workload) and resident in HBM before timing starts.
 
 Prints one JSON line. `value` = tokens per second of the whole step (16384 / step time).
-`roofline` describes the dominant part, the chunked prefill (one kda_prefill call: its plan,
+`roofline` describes the dominant part, the chunked prefill (one kda_prefill call: its
 chunk_prep and state_pass kernels), timed with HIP events on the stream the library launches
 on, in a second timed pass that issues the same calls one by one. `cpu_baseline` times the CPU
 oracle on a bounded sample (a subset of heads).
@@ -41,17 +41,15 @@ TOK_OUT_B = D * 2                           # o bf16
 RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
 
 
-# HBM traffic of one prefill call of the mixed step (its three kernels: plan, chunk_prep,
-# state_pass), from rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch)
+# HBM traffic of one prefill call of the mixed step (its two kernels: chunk_prep, which plans a
+# batch of this size itself, and state_pass), from rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch)
 # scaled by the counters' reading for a 1 GiB device copy (FETCH_SIZE reads half the copied
 # bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid only for the kernel source it was
 # measured on (first 16 hex digits of its SHA-256); for any other source the bench reports
 # traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "12fa5babe31142fb", "fetch_scale": 2.0, "write_scale": 1.0,
-                   "fetch_kib": {"prefill_plan_kernel": 5, "chunk_prep_kernel": 269324,
-                                 "state_pass_kernel<4, 1, 4>": 316062},
-                   "write_kib": {"prefill_plan_kernel": 0, "chunk_prep_kernel": 501746,
-                                 "state_pass_kernel<4, 1, 4>": 142818}}
+PREFILL_TRAFFIC = {"source_sha256_16": "ac6965ccf7cf6513", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"chunk_prep_kernel": 269336, "state_pass_kernel<4, 1, 4>": 316059},
+                   "write_kib": {"chunk_prep_kernel": 501491, "state_pass_kernel<4, 1, 4>": 142818}}
 
 
 def prefill_traffic_bytes():
@@ -254,7 +252,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": prefill_traffic_bytes(),
                 "kernel": "prefill: one kda_prefill call over all sequences of the batch "
-                          "(plan, chunk_prep and state_pass kernels, back to back on one stream)",
+                          "(chunk_prep and state_pass kernels, back to back on one stream)",
                 "alg_bytes_per_launch": byts["prefill"]}
 
     cpu = None
