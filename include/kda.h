@@ -142,6 +142,16 @@ typedef struct {
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
                                    int32_t chunk, int32_t ckpt_interval);
 kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);
+/* Width plan of kda_prefill's sequential (inter-chunk) pass for sequences with host lengths
+ * h_cu_seqlens[0..n_seq] on the current device (the chunked form, dk = 128): returns the number
+ * of groups G (1..4) and fills rank_end[0..G-1] and vsw[0..G-1] (caller arrays of 4): the
+ * sequences ranked rank_end[i-1] .. rank_end[i] - 1 by length (longest first, ties: lower index
+ * first; rank_end[-1] = 0) run in work-groups of vsw[i] value columns (16, 32, 64 or 128).
+ * Long chains take narrow slices, short ones wide slices, by a latency / CU-time model; one
+ * group beyond 64 sequences, and kda_mixed_batch always uses one group. Host only; returns 0
+ * for a null argument or n_seq <= 0.                                                         */
+int32_t kda_prefill_plan(const kda_pool* pool, int32_t n_seq, const int32_t* h_cu_seqlens,
+                         int32_t* rank_end, int32_t* vsw);
 
 /* ---- decode and speculative verify ---------------------------------------------------- */
 /* Token tensors are [B][n_pos][H][d] (n_pos = 1 for decode); slots[B] are live, idle and

@@ -27,6 +27,15 @@ struct StepTensors {
   uint16_t* o;
 };
 
+// Width plan of the prefill's sequential pass: the sequences ranked rank_end[g - 1] ..
+// rank_end[g] - 1 by length (rank_end[-1] = 0) run in work-groups of vsw[g] value columns
+// (16, 32, 64 or 128), work-groups wg_begin[g] .. wg_begin[g + 1] - 1 (each group a multiple of
+// 8), groups in rank order so that the longest sequences' work-groups are dispatched first.
+struct StatePlan {
+  int32_t n_groups;
+  int32_t rank_end[4], vsw[4], wg_begin[5];
+};
+
 struct PrefillLaunch {
   StepTensors t;
   int32_t n_seq, n_tok, chunk, ckpt_interval;
@@ -37,6 +46,7 @@ struct PrefillLaunch {
   int32_t max_len;             // longest sequence (host-known), sizes the grid
   int64_t n_chunks;            // sum over sequences of ceil(len / chunk) (host-known)
   void* workspace;             // device, at least prefill_workspace_bytes(...) bytes
+  StatePlan plan;              // from plan_state_pass (host lengths)
 };
 
 hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B,
@@ -65,6 +75,14 @@ struct PrefillHook {
 };
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s,
                           const PrefillHook* after_prep = nullptr);
+// Width plan for the sequential pass of a prefill with host lengths h_cu[0..n_seq]. Long
+// chains take narrow slices (a chunk's latency falls with fewer compute waves sharing a CU's
+// LDS), short ones wide slices (fewer work-groups, each CU-cheaper per column), chosen by a
+// latency / CU-time model of the pass; beyond 64 sequences, and with shared (independent work
+// runs next to the pass, as in a mixed batch), one width for all: there the other work needs the
+// CUs that the short chains free, and the long chains slow under its HBM traffic, which the
+// model leaves out.
+StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H, bool shared);
 // Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
 // shapes that run the token-by-token kernel).
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);

@@ -238,6 +238,17 @@ kda_status kda_slot_free(kda_pool* p, int32_t s) {
   return KDA_OK;
 }
 
+int32_t kda_prefill_plan(const kda_pool* p, int32_t n_seq, const int32_t* h_cu, int32_t* rank_end,
+                         int32_t* vsw) {
+  if (!p || !h_cu || !rank_end || !vsw || n_seq <= 0) return 0;
+  const kda::StatePlan sp = kda::plan_state_pass(h_cu, n_seq, p->desc.num_heads, false);
+  for (int32_t g = 0; g < sp.n_groups; ++g) {
+    rank_end[g] = sp.rank_end[g];
+    vsw[g] = sp.vsw[g];
+  }
+  return sp.n_groups;
+}
+
 int32_t kda_slot_host_state(const kda_pool* p, int32_t s) {
   if (!p || s < 0 || s >= p->desc.num_slots) return -1;
   return p->slot_state[s];
@@ -377,6 +388,7 @@ kda_status kda_prefill(kda_pool* p, const kda_prefill_args* a, void* stream) {
   kda::PrefillLaunch L{tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->n_seq, a->n_tok,
                        a->chunk, a->ckpt_interval, a->d_cu_seqlens, a->d_init_slot,
                        a->d_out_slot, a->d_ckpt_slot, max_len, n_chunks, ws};
+  L.plan = kda::plan_state_pass(a->h_cu_seqlens, a->n_seq, p->desc.num_heads, false);
   hipError_t e = kda::launch_prefill(p->view, L, as_stream(stream));
   return e == hipSuccess ? KDA_OK : hip_fail(e, "prefill launch");
 }
@@ -542,6 +554,7 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     kda::PrefillLaunch L{part(0), pre.n_seq, pre.n_tok, pre.chunk, pre.ckpt_interval,
                          pre.d_cu_seqlens, pre.d_init_slot, pre.d_out_slot, pre.d_ckpt_slot,
                          max_len, n_chunks, ws};
+    L.plan = kda::plan_state_pass(pre.h_cu_seqlens, pre.n_seq, H, sl.fork);
     const kda::PrefillHook hook{&StepLaunches::forked, &sl};
     e = kda::launch_prefill(p->view, L, s, sl.fork ? &hook : nullptr);
     if (e != hipSuccess) return hip_fail(e, "mixed: prefill launch");

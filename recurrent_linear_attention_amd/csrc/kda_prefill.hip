@@ -640,14 +640,23 @@ struct StateFetch {
 // it in issue order; the prologue issues kv(0), qta(0), kbg(0), kv(1), qta(1), which gives the
 // same counts from chunk 0 on). Lanes 0-31 of load wave 0 also load 2^(G_C) in each kbg group:
 // the counts leave that load out, so that wave waits for slightly more than it needs.
-template <int CW, int TPW, int LW>
-__global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, PrefillLaunch A,
-                                                         const int32_t* __restrict__ choff,
-                                                         const int32_t* __restrict__ ckoff,
-                                                         const int32_t* __restrict__ order,
-                                                         const char* __restrict__ blocks, int n_hg) {
-  constexpr int VSW = 16 * CW * TPW;        // value columns per work-group
-  constexpr int NVS = PD / VSW;
+// A state-pass work-group has SCW compute waves (one per 16-column tile of a 128-column slice)
+// and SLW load waves; a work-group on a narrower slice ends its surplus compute waves at once
+// (a barrier counts only the waves still running).
+constexpr int SCW = PD / 16;
+constexpr int SLW = 4;
+
+// The pass of (sequence, head) chain hg (rank hg / H by length, head hg % H) over value
+// columns [VSW vs, VSW (vs + 1)), on the work-group's LDS (two chunk images of StateBuf<VSW>).
+template <int VSW>
+__device__ __forceinline__ void state_pass_body(const PoolView& P, const PrefillLaunch& A,
+                                                const int32_t* __restrict__ choff,
+                                                const int32_t* __restrict__ ckoff,
+                                                const int32_t* __restrict__ order,
+                                                const char* __restrict__ blocks, int hg, int vs,
+                                                int wave, char* lds_base) {
+  constexpr int TPW = 1;                    // 16-column tiles per compute wave
+  constexpr int LW = SLW;
   constexpr int NTL = 64 * LW;              // load-issuing threads
   using SB = StateBuf<VSW, NTL>;
   using SF = StateFetch<VSW, NTL>;
@@ -656,16 +665,10 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   constexpr int WAIT_BW = N_KBG + SF::N_KV + SF::N_QTA + N_KBG;
   constexpr int WAIT_BS = SF::N_KV + SF::N_QTA + N_KBG + SF::N_KV;
   static_assert(WAIT_BX <= 63 && WAIT_BW <= 63 && WAIT_BS <= 63, "vmcnt holds at most 63");
-  __shared__ __attribute__((aligned(16))) char lds[2][SB::BYTES];
-  const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3;
-  const int vs = m % NVS, hg = (m / NVS) * 8 + xcd;
-  if (hg >= n_hg) return;
   const int H = P.H, h = hg % H, si = order[hg / H];
-  // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar.
-  // Load waves are waves CW .. CW + LW - 1; t and w index within a role.
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const bool loads = wave >= CW;
-  const int w = loads ? wave - CW : wave, t = (int)threadIdx.x - 64 * (wave - w),
+  // Load waves are waves SCW .. SCW + LW - 1; t and w index within a role.
+  const bool loads = wave >= SCW;
+  const int w = loads ? wave - SCW : wave, t = (int)threadIdx.x - 64 * (wave - w),
             l = t & 63, l16 = l & 15, lq = l >> 4;
 
   const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   const int colw = col0 + cw;
   const int hst2 = H * PD * 2;
   const char* blk0 = blocks + ((size_t)choff[si] * H + h) * BLOCK_BYTES;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0][0], lds1 = (uint32_t)(uintptr_t)&lds[1][0];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds_base, lds1 = lds0 + SB::BYTES;
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
   const int nlast = nch - 1;
   auto sf = [&](int c) __attribute__((always_inline)) {   // past the last chunk: repeat it
@@ -747,7 +750,7 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
     int t0, n;
     chunk_span(c, len, PC, A.ckpt_interval, &t0, &n);
     const int tok0 = lo + t0;
-    const char* buf = lds[c & 1];
+    const char* buf = lds_base + (c & 1) * SB::BYTES;
     const _Float16* bh = reinterpret_cast<const _Float16*>(buf);
     const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + BLOCK_BYTES);
     auto frag = [&](int off, int f) __attribute__((always_inline)) {
@@ -916,6 +919,35 @@ __global__ __launch_bounds__(64 * (CW + LW)) void state_pass_kernel(PoolView P, 
   }
 }
 
+// Work-group bid of the pass: its group g in the width plan (groups run longest sequences
+// first), then within the group the slices of a head sit on one XCD (block index mod 8) so that
+// they share L2 for the operand blocks.
+__global__ __launch_bounds__(64 * (SCW + SLW)) void state_pass_kernel(PoolView P, PrefillLaunch A,
+                                                                     const int32_t* __restrict__ choff,
+                                                                     const int32_t* __restrict__ ckoff,
+                                                                     const int32_t* __restrict__ order,
+                                                                     const char* __restrict__ blocks) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * StateBuf<PD, 64 * SLW>::BYTES];
+  const StatePlan& sp = A.plan;
+  const int bid = blockIdx.x;
+  int g = 0;
+  while (g + 1 < sp.n_groups && bid >= sp.wg_begin[g + 1]) ++g;
+  const int vsw = sp.vsw[g], nvs = PD / vsw, r0 = g > 0 ? sp.rank_end[g - 1] : 0;
+  const int lb = bid - sp.wg_begin[g], xcd = lb & 7, m = lb >> 3;
+  const int hgl = (m / nvs) * 8 + xcd;
+  if (hgl >= (sp.rank_end[g] - r0) * P.H) return;
+  // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (wave < SCW && wave >= vsw / 16) return;
+  const int hg = r0 * P.H + hgl, vs = m % nvs;
+  switch (vsw) {
+    case 16: state_pass_body<16>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
+    case 32: state_pass_body<32>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
+    case 64: state_pass_body<64>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
+    default: state_pass_body<128>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
+  }
+}
+
 int device_cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -932,18 +964,17 @@ int device_cu_count() {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
 
-template <int CW, int TPW, int LW>
 hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
                         const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
-  const int n_hg = a.n_seq * p.H;
-  const int nb = ((n_hg + 7) / 8) * 8 * (PD / (16 * CW * TPW));
+  const int nb = a.plan.wg_begin[a.plan.n_groups];
+  if (nb <= 0) return hipSuccess;
   // The rest of the CU's LDS is requested too (unused), so that no other work-group shares a CU
   // with a state-pass work-group: in a mixed batch the decode and verify kernels on the side
   // stream then run on the CUs the pass leaves free instead of slowing its sequential chain.
-  constexpr int lds_static = 2 * StateBuf<16 * CW * TPW, 64 * LW>::BYTES;
+  constexpr int lds_static = 2 * StateBuf<PD, 64 * SLW>::BYTES;
   static_assert(lds_static <= LDS_PER_CU, "state pass LDS image");
-  hipLaunchKernelGGL((state_pass_kernel<CW, TPW, LW>), dim3(nb), dim3(64 * (CW + LW)),
-                     LDS_PER_CU - lds_static, s, p, a, choff, ckoff, order, blocks, n_hg);
+  hipLaunchKernelGGL(state_pass_kernel, dim3(nb), dim3(64 * (SCW + SLW)), LDS_PER_CU - lds_static, s, p,
+                     a, choff, ckoff, order, blocks);
   return hipGetLastError();
 }
 
@@ -986,13 +1017,91 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     e = after_prep->fn(after_prep->ctx);
     if (e != hipSuccess) return e;
   }
-  // The narrowest slices whose grid fits in one round of CUs: a chain's latency per chunk falls
-  // with fewer compute waves per CU (less LDS traffic each), while more work-groups per head
-  // only pay off while CUs would otherwise idle. Larger batches take 64-column slices.
-  const int n_hg = a.n_seq * p.H, cus = device_cu_count();
-  if (n_hg * 8 <= cus) return launch_state<1, 1, 4>(p, a, choff, ckoff, order, blocks, s);
-  if (n_hg * 4 <= cus) return launch_state<2, 1, 4>(p, a, choff, ckoff, order, blocks, s);
-  return launch_state<4, 1, 4>(p, a, choff, ckoff, order, blocks, s);
+  return launch_state(p, a, choff, ckoff, order, blocks, s);
+}
+
+StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H, bool shared) {
+  // Per-chunk latency of one chain (us) with 16, 32, 64 and 128 value columns per work-group,
+  // measured on MI355X for the mixed 16384-token batch, plus a work-group's start-up; the pass
+  // keeps one work-group per CU, and list scheduling in rank order packs CU-time to ~85%.
+  constexpr float LAT[4] = {1.55f, 1.8f, 2.3f, 3.1f};
+  constexpr float START = 3.f, PACK = 0.85f;
+  constexpr int WIDTH[4] = {16, 32, 64, 128};
+  const int cus = device_cu_count();
+  auto build = [&](int n_groups, const int* ends, const int* widths) {
+    StatePlan sp{};
+    sp.n_groups = n_groups;
+    int begin = 0, r0 = 0;
+    for (int g = 0; g < n_groups; ++g) {
+      sp.rank_end[g] = ends[g];
+      sp.vsw[g] = widths[g];
+      sp.wg_begin[g] = begin;
+      begin += ((ends[g] - r0) * H + 7) / 8 * 8 * (PD / widths[g]);
+      r0 = ends[g];
+    }
+    sp.wg_begin[n_groups] = begin;
+    return sp;
+  };
+  // one width for all: the narrowest whose grid fits in one round of CUs, else 64 columns
+  const int n_hg = n_seq * H;
+  const int wu = n_hg * 8 <= cus ? 0 : (n_hg * 4 <= cus ? 1 : 2);
+  const int end_all[1] = {n_seq}, w_all[1] = {WIDTH[wu]};
+  const StatePlan uniform = build(1, end_all, w_all);
+  if (shared || n_seq < 2 || n_seq > PLAN_INLINE_MAX) return uniform;
+  // chunk counts in rank order: descending length, ties lower index first (the plan's order)
+  int idx[PLAN_INLINE_MAX], nch[PLAN_INLINE_MAX];
+  for (int i = 0; i < n_seq; ++i) idx[i] = i;
+  auto len = [&](int i) { return h_cu[i + 1] - h_cu[i]; };
+  std::stable_sort(idx, idx + n_seq, [&](int x, int y) { return len(x) > len(y); });
+  for (int r = 0; r < n_seq; ++r) nch[r] = seq_chunks(len(idx[r]), PC, 0);
+  auto predict = [&](const int* wi) {
+    float chain = 0.f, cu_time = 0.f;
+    int64_t wgs = 0;
+    for (int r = 0; r < n_seq; ++r) {
+      const float t = nch[r] * LAT[wi[r]] + START;
+      const int slices = PD / WIDTH[wi[r]];
+      chain = std::max(chain, t);
+      cu_time += (float)H * slices * t;
+      wgs += (int64_t)H * slices;
+    }
+    return wgs <= cus ? chain : std::max(chain, cu_time / (PACK * cus));
+  };
+  int wi[PLAN_INLINE_MAX], best[PLAN_INLINE_MAX];
+  for (int r = 0; r < n_seq; ++r) wi[r] = wu;
+  const float t_uniform = predict(wi);
+  float t_best = t_uniform;
+  bool found = false;
+  // each candidate bounds every chain by one chain's time at one width; each rank then takes
+  // the widest slices that stay within it (non-decreasing along the ranks)
+  for (int rr = 0; rr < n_seq; ++rr)
+    for (int ww = 0; ww < 4; ++ww) {
+      const float bound = nch[rr] * LAT[ww] + START;
+      bool ok = true;
+      for (int r = 0; r < n_seq && ok; ++r) {
+        int w = 3;
+        while (w >= 0 && nch[r] * LAT[w] + START > bound) --w;
+        if (w < 0) ok = false;
+        wi[r] = w;
+      }
+      if (!ok) continue;
+      const float t = predict(wi);
+      if (t < t_best) {
+        t_best = t;
+        found = true;
+        std::copy(wi, wi + n_seq, best);
+      }
+    }
+  // a different plan only for a clear predicted gain (the model is coarse)
+  if (!found || t_best > 0.95f * t_uniform) return uniform;
+  int ends[4], widths[4], n_groups = 0;
+  for (int r = 0; r < n_seq; ++r) {
+    if (n_groups == 0 || WIDTH[best[r]] != widths[n_groups - 1]) {
+      if (n_groups == 4) return uniform;
+      widths[n_groups++] = WIDTH[best[r]];
+    }
+    ends[n_groups - 1] = r + 1;
+  }
+  return build(n_groups, ends, widths);
 }
 
 }  // namespace kda

@@ -285,6 +285,15 @@ class KDAPool:
         check(lib.kda_mixed_batch(self.handle, byref(m), _stream(stream)), "kda_mixed_batch")
         return o
 
+    def kda_prefill_plan(self, cu_seqlens) -> list:
+        """Width plan of kda_prefill's state pass for these sequence boundaries:
+        [(rank_end, value_columns), ...] over the sequences ranked by length."""
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        ends, vsw = np.zeros(4, np.int32), np.zeros(4, np.int32)
+        n = lib.kda_prefill_plan(self.handle, cu.size - 1, cu.ctypes.data, ends.ctypes.data,
+                                 vsw.ctypes.data)
+        return [(int(ends[i]), int(vsw[i])) for i in range(n)]
+
     def kda_read_device_error(self, stream=None) -> int:
         bits = c_uint32()
         check(lib.kda_read_device_error(self.handle, byref(bits), _stream(stream)),

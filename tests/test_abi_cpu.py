@@ -282,3 +282,32 @@ def test_prefix_hit_policy():
              ((64, 65, 64), 64), ((64, 64, 64), 0), ((10, 10, 0), 0), ((-3, 10, 4), 0)]
     for args, want in cases:
         assert prefix_hit(*args) == want, (args, want)
+
+
+def plan_of(lengths, H=32):
+    p = HostPool(n=8, H=H, d=128)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ends, vsw = np.zeros(4, np.int32), np.zeros(4, np.int32)
+    n = lib.kda_prefill_plan(p.h, len(lengths), cu.ctypes.data, ends.ctypes.data, vsw.ctypes.data)
+    return [(int(ends[i]), int(vsw[i])) for i in range(n)]
+
+
+def test_prefill_width_plan():
+    """State-pass width plan on a 256-CU part (the CU count this container's library falls
+    back to without a device): one width while every chain is about as long as the rest
+    (the narrowest whose grid fits in one round of CUs, else 64 columns), narrow slices for
+    long chains and 128-column slices for short ones in a lognormal mix; groups cover the
+    ranks in order."""
+    assert plan_of([8192]) == [(1, 16)]
+    assert plan_of([5719, 4580]) == [(2, 32)]
+    assert plan_of([2048] * 4) == [(4, 64)]
+    assert plan_of([1024] * 8) == [(8, 128)]
+    assert plan_of([512] * 32) == [(32, 128)]
+    assert plan_of([1423, 1318, 1801, 1475, 4580, 5719]) == [(1, 32), (2, 64), (6, 128)]
+    assert plan_of([300, 8000, 200, 100, 50, 10]) == [(1, 32), (6, 128)]
+    assert plan_of([100] * 65) == [(65, 64)]                 # beyond 64 sequences: one width
+    assert plan_of([0, 0, 0]) == [(3, 64)]                   # no chunk: no gain, one width
+    p = HostPool(n=8, H=32, d=128)
+    z = np.zeros(4, np.int32)
+    assert lib.kda_prefill_plan(p.h, 0, z.ctypes.data, z.ctypes.data, z.ctypes.data) == 0
+    assert lib.kda_prefill_plan(p.h, 1, None, z.ctypes.data, z.ctypes.data) == 0

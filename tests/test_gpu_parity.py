@@ -555,6 +555,46 @@ def test_prefill_one_long_and_five_short():
     assert g.kda_read_device_error() == 0
 
 
+
+@pytest.mark.parametrize("lengths,plan", [
+    ([1024] * 8, [(8, 128)]),
+    ([300, 8000, 200, 100, 50, 10], [(1, 32), (6, 128)]),
+    ([1423, 1318, 1801, 1475, 4580, 5719], [(1, 32), (2, 64), (6, 128)]),
+])
+def test_prefill_planned_slice_widths(lengths, plan):
+    """Batches whose state pass runs one, two and three groups of slice widths in one launch
+    (longest sequences in the narrowest slices, short ones in 128-column work-groups): the
+    plan the library reports, and outputs, final and checkpoint states of sampled heads against
+    the oracle, with a resumed sequence and checkpoints every 1024 tokens."""
+    rng = np.random.default_rng(sum(lengths) % 1000)
+    H, d, interval = 32, 128, 1024
+    n_seq = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    n_ck = sum(L // interval for L in lengths)
+    n_slots = n_seq + n_ck + 1
+    g, _ = pools(n_slots, H, d)
+    assert g.kda_prefill_plan(cu) == plan
+    st = ki.draw_states(rng, 1, H, d, d)
+    g.state[n_slots - 1] = st[0].to("cuda")
+    init = [-1] * n_seq
+    init[n_seq - 1] = n_slots - 1
+    out = list(range(n_seq))
+    cks = list(range(n_seq, n_seq + n_ck))
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks, ckpt_interval=interval)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    o = OPool(n_slots, len(heads), d, d, 9)
+    for _ in range(n_slots):
+        o.alloc()
+    o.state[n_slots - 1] = st[0][heads].double().numpy()
+    Oo = o.prefill(heads_np(tok, heads), cu, init, out, cks, interval)
+    assert rel_bf16(O[:, heads], Oo) <= TOL
+    for s_ in out + cks:
+        assert rel(g.state[s_][heads], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), out + cks)
+    assert g.kda_read_device_error() == 0
+
 def test_prefill_with_pool_owned_workspace():
     """workspace = NULL through the C ABI: the pool allocates its own (and grows it for a
     larger call); results are bit-identical to those with the caller's workspace."""
