@@ -365,17 +365,20 @@ def test_prefill_checkpoints_at_unaligned_intervals(d, interval):
     assert g.kda_read_device_error() == 0
 
 
-@pytest.mark.parametrize("H,n_seq", [(4, 7), (32, 2), (32, 3), (32, 9)])
-def test_prefill_every_slice_width(H, n_seq):
-    """sequences x heads of 28, 64 and 96 / 288 run the state pass with 16-, 32- and 64-column
-    slices (on a 256-CU part); each must match the oracle (sampled heads, ragged lengths, a
-    resumed first sequence, checkpoints)."""
+@pytest.mark.parametrize("H,n_seq,plan", [(4, 7, [(7, 16)]), (32, 2, [(2, 32)]),
+                                           (32, 3, [(1, 32), (2, 64), (3, 128)]),
+                                           (32, 9, [(9, 128)])])
+def test_prefill_every_slice_width(H, n_seq, plan):
+    """Small ragged batches whose state pass runs 16-, 32-, 64- and 128-column slices (on a
+    256-CU part; the plan the library reports is pinned); each must match the oracle (sampled
+    heads, a resumed first sequence, checkpoints)."""
     rng = np.random.default_rng(60 + H + n_seq)
     lengths = [int(x) for x in rng.integers(1, 300, size=n_seq)]
     lengths[0] = 257
     d = 128
     g, _ = pools(32, H, d)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    assert g.kda_prefill_plan(cu) == plan
     tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
     init = [-1] * n_seq
     init[0] = 31
