@@ -191,6 +191,52 @@ __device__ __forceinline__ void store_state(const float (&S)[C::RPT][4], float* 
 
 __device__ __forceinline__ int wrap(int x, int R) { return ((x % R) + R) % R; }
 
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// Stores through a buffer resource over [base, base + bytes) whose lanes opt out with an
+// offset past the range (the hardware drops them): every wave issues the same store
+// instructions whatever its lanes' roles, so a loop that prefetches its next position's inputs
+// before these stores waits only for those loads (a fixed count of later operations), not
+// for the stores to retire.
+struct MaskedStore {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t oob;
+  __device__ __forceinline__ MaskedStore(const void* base, uint32_t bytes)
+      : rs(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)),
+        oob(bytes) {}
+  __device__ __forceinline__ uint32_t at(bool on, uint32_t byte_off) const { return on ? byte_off : oob; }
+  template <int N>   // N raw bf16 words (N = 1, 4 or 8)
+  __device__ __forceinline__ void bf16(bool on, uint32_t off, const uint32_t (&w)[(N + 1) / 2]) const {
+    const uint32_t o = at(on, off);
+    if constexpr (N == 1) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[0], rs, o, 0, 0);
+    } else if constexpr (N == 4) {
+      __builtin_amdgcn_raw_buffer_store_b64(u2v{w[0], w[1]}, rs, o, 0, 0);
+    } else {
+      static_assert(N % 8 == 0, "bf16 vector width");
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(u4v{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]}, rs,
+                                               at(on, off + 16 * i), 0, 0);
+    }
+  }
+  template <int N>   // N floats (N = 1 or a multiple of 4)
+  __device__ __forceinline__ void f32(bool on, uint32_t off, const float (&f)[N]) const {
+    if constexpr (N == 1) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f[0]), rs, at(on, off), 0, 0);
+    } else {
+      static_assert(N % 4 == 0, "float vector width");
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u4v{__float_as_uint(f[4 * i]), __float_as_uint(f[4 * i + 1]), __float_as_uint(f[4 * i + 2]),
+                __float_as_uint(f[4 * i + 3])},
+            rs, at(on, off + 16 * i), 0, 0);
+    }
+  }
+};
+
 // An empty use of every state register: the compiler places the wait for the state loads here,
 // before a loop over positions, instead of at their first use inside the loop, where it would
 // also wait for the next position's prefetched inputs on every iteration.
@@ -260,24 +306,29 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
   StepRaw<C> nxt;
   fetch(nxt, 0);
   state_ready<C>(S);
+  // outputs of this sequence and head (rows j of n_pos), and the slot's ring for this head
+  // (entries wrap(head + j, R) of R): byte ranges small enough for 32-bit buffer offsets
+  const size_t HD = (size_t)P.H * D;
+  const MaskedStore so(T.o + ((size_t)bi * n_pos * P.H + h) * D, (uint32_t)(n_pos * HD * 2));
+  const size_t ring0 = ((size_t)slot * R * P.H + h) * D;
+  const MaskedStore sk(P.ring_k + ring0, (uint32_t)(R * HD * 2)), sv(P.ring_v + ring0, (uint32_t)(R * HD * 2));
+  const MaskedStore sa(P.ring_a + ring0, (uint32_t)(R * HD * 4));
+  const MaskedStore sb(P.ring_b + (size_t)slot * R * P.H + h, (uint32_t)(R * P.H * 4));
+  const bool out_lane = rg == 0, key_lane = vs == 0 && cg == 0, b_lane = key_lane && t == 0;
   for (int j = 0; j < n_pos; ++j) {
-    const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
     StepIn<C> in;
     unpack_in<C, true>(in, nxt);
     if (j + 1 < n_pos) fetch(nxt, j + 1);
     float o[4];
     step<C, true>(S, in, lds, j & 1, o);
-    const size_t e = ((size_t)slot * R + (size_t)wrap(head + j, R)) * P.H + h;
-    if (rg == 0) {
-      uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
-      store_bf16_raw<4>(T.o + row * D + c0, ow);
-      store_bf16_raw<4>(P.ring_v + e * D + c0, in.vw);
-    }
-    if (vs == 0 && cg == 0) {
-      store_bf16_raw<C::RPT>(P.ring_k + e * D + r0, in.kw);
-      store_f32<C::RPT>(P.ring_a + e * D + r0, in.a);
-      if (t == 0) P.ring_b[e] = in.b;
-    }
+    const uint32_t er = (uint32_t)wrap(head + j, R) * (uint32_t)HD;   // ring entry, elements
+    const uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+    so.bf16<4>(out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
+    sv.bf16<4>(out_lane, (er + c0) * 2, in.vw);
+    sk.bf16<C::RPT>(key_lane, (er + r0) * 2, in.kw);
+    sa.f32<C::RPT>(key_lane, (er + r0) * 4, in.a);
+    const float bv[1] = {in.b};
+    sb.f32<1>(b_lane, (uint32_t)wrap(head + j, R) * (uint32_t)P.H * 4, bv);
   }
   if (t == 0 && h == 0 && vs == 0) {
     P.meta[slot].v_base = head;
