@@ -688,6 +688,39 @@ def test_mixed_batch_full_size_sampled():
     assert g.kda_read_device_error() == 0
 
 
+
+def test_mixed_batch_many_prefills():
+    """A mixed batch with 70 prompts (more than the operand kernel plans itself: the plan
+    kernel runs on the caller's stream) next to decodes and a verify on the side stream:
+    every part against the oracle, all heads (H = 4, short ragged prompts)."""
+    rng = np.random.default_rng(123)
+    H, d, P = 4, 128, 3
+    lengths = [int(x) for x in rng.choice([0, 1, 7, 64, 65, 200], size=70)]
+    n_dec, n_ver = 5, 2
+    n_slots = 70 + n_dec + n_ver
+    g, o = pools(n_slots, H, d, R=P)
+    ps = np.arange(70)
+    ds = np.arange(70, 70 + n_dec)
+    vs = np.arange(70 + n_dec, n_slots)
+    put_states(g, o, np.concatenate([ds, vs]), ki.draw_states(rng, n_dec + n_ver, H, d, d))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    n_pre = int(cu[-1])
+    tok = ki.draw_tokens(rng, (n_pre + n_dec + n_ver * P,), H, d, d)
+    O = g.kda_mixed_batch(*tok_dev(tok), cu, ps, ds, vs, P)
+    torch.cuda.synchronize()
+    Op = o.prefill(tok.slice(0, n_pre).np, cu, [-1] * 70, ps, [], 0)
+    Od = o.decode(tok.slice(n_pre, n_pre + n_dec).np, ds)
+    vt = {n: x[n_pre + n_dec:].reshape((n_ver, P) + x.shape[1:]) for n, x in tok.np.items()}
+    Ov = o.verify(vt, vs)
+    assert rel_bf16(O[:n_pre], Op) <= TOL
+    assert rel_bf16(O[n_pre:n_pre + n_dec], Od) <= TOL
+    assert rel_bf16(O[n_pre + n_dec:].reshape(n_ver, P, H, d), Ov) <= TOL
+    for s_ in np.concatenate([ps, ds]):
+        assert rel(g.state[int(s_)], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), np.arange(n_slots))
+    ring_check(g, o, vs)
+    assert g.kda_read_device_error() == 0
+
 def test_mixed_batch_commits_previous_verify():
     """Two serving steps: the second mixed batch commits the first one's verified drafts (its
     commit part) before verifying the same slots again, next to a new prefill and decodes.
