@@ -20,8 +20,13 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
+// Two fp32 values -> packed bf16 (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (equal to f2bf for every non-NaN input).
+typedef __bf16 kda_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float kda_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  const kda_f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, kda_bf16x2));
 }
 
 // Load N consecutive bf16 values as raw 16-bit words (N in {1, 2, 4, 8, 16}); the pointer

@@ -53,11 +53,36 @@ struct StepLds {
   float red[2][C::NW][2 * C::VS + 4];
 };
 
+// x + the value of lane l ^ 8 (DPP row_ror:8 inside each 16-lane row: a VALU operand
+// modifier, no LDS round trip).
+__device__ __forceinline__ float add_xor8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// x + the value of lane l ^ 16 / l ^ 32. With both operands equal, v_permlane16_swap returns
+// (row 2r, row 2r) and (row 2r + 1, row 2r + 1) of x for each pair of 16-lane rows, and
+// v_permlane32_swap the lower and the upper half-wave: the sum of the pair is the same in both
+// lanes of a pair.
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Sum over the lanes of a wave that hold the same value columns (lanes l ^ TPR, l ^ 2 TPR, ..).
+// Each level adds a lane and its partner, so both lanes of a pair get the same bits.
 template <class C>
 __device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (C::TPR == 8) {
+    return add_xor32(add_xor16(add_xor8(x)));
+  } else {
 #pragma unroll
-  for (int m = C::TPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+    for (int m = C::TPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+  }
 }
 
 // One position of the rule on the thread's RPT x 4 tile. WITH_O also produces o for the
@@ -191,6 +216,12 @@ __device__ __forceinline__ void store_state(const float (&S)[C::RPT][4], float* 
 
 __device__ __forceinline__ int wrap(int x, int R) { return ((x % R) + R) % R; }
 
+// Ring entry j after entry `base` (0 <= base < R, 0 <= j <= R): one compare, no division.
+__device__ __forceinline__ int ring_at(int base, int j, int R) {
+  const int e = base + j;
+  return e >= R ? e - R : e;
+}
+
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
@@ -248,6 +279,36 @@ __device__ __forceinline__ void state_ready(const float (&S)[C::RPT][4]) {
     for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(S[r][c]));
 }
 
+// Steps positions 0..n-1 (n >= 1) with the next position's inputs in flight. The inputs
+// alternate between two register buffers and the loop covers two positions per trip, so no
+// buffer is ever copied: one buffer carried around the loop would be moved into place on every
+// trip, and those moves wait for the loads in flight. Both positions of a trip issue the same
+// memory operations whatever n is -- a fetch past the end re-reads position n - 1, and for an
+// odd n the trip's second position is a padding position j = n, where `body` must neither step
+// nor store anything visible -- so the compiler can count the operations issued after each
+// buffer's loads and waits for those loads only. The state and the first position's inputs are
+// waited for at once: nothing is in flight when the loop is entered, so the waits inside it
+// follow the loop's own pattern.
+template <class C, bool WITH_Q, class Fetch, class Body>
+__device__ __forceinline__ void stepped_positions(int n, float (&S)[C::RPT][4], const float* Sp, int r0,
+                                                  int c0, Fetch&& fetch, Body&& body) {
+  StepRaw<C> b0, b1;
+  fetch(b0, 0);
+  load_state<C>(S, Sp, r0, c0);
+  __builtin_amdgcn_s_waitcnt(0);   // position 0 needs both
+  state_ready<C>(S);
+  auto one = [&](int j, const StepRaw<C>& cur, StepRaw<C>& nxt) {
+    StepIn<C> in;
+    unpack_in<C, WITH_Q>(in, cur);
+    fetch(nxt, j + 1 < n ? j + 1 : n - 1);
+    body(j, in);
+  };
+  for (int j = 0; j < n; j += 2) {
+    one(j, b0, b1);
+    one(j + 1, b1, b0);
+  }
+}
+
 // grid: B * H * (D / VS); block (bi, h, vs) with vs fastest.
 template <int D>
 __global__ __launch_bounds__(StepCfg<D>::NT) void decode_kernel(PoolView P, StepTensors T,
@@ -298,14 +359,10 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
   const int head = wrap(P.meta[slot].ring_head, R);
   const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
   float S[C::RPT][4];
-  load_state<C>(S, Sp, r0, c0);
   auto fetch = [&](StepRaw<C>& r, int j) {
     const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
     fetch_in<C, true>(r, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
   };
-  StepRaw<C> nxt;
-  fetch(nxt, 0);
-  state_ready<C>(S);
   // outputs of this sequence and head (rows j of n_pos), and the slot's ring for this head
   // (entries wrap(head + j, R) of R): byte ranges small enough for 32-bit buffer offsets
   const size_t HD = (size_t)P.H * D;
@@ -315,21 +372,20 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
   const MaskedStore sa(P.ring_a + ring0, (uint32_t)(R * HD * 4));
   const MaskedStore sb(P.ring_b + (size_t)slot * R * P.H + h, (uint32_t)(R * P.H * 4));
   const bool out_lane = rg == 0, key_lane = vs == 0 && cg == 0, b_lane = key_lane && t == 0;
-  for (int j = 0; j < n_pos; ++j) {
-    StepIn<C> in;
-    unpack_in<C, true>(in, nxt);
-    if (j + 1 < n_pos) fetch(nxt, j + 1);
-    float o[4];
-    step<C, true>(S, in, lds, j & 1, o);
-    const uint32_t er = (uint32_t)wrap(head + j, R) * (uint32_t)HD;   // ring entry, elements
+  stepped_positions<C, true>(n_pos, S, Sp, r0, c0, fetch, [&](int j, const StepIn<C>& in) {
+    const bool live = j < n_pos;   // false only at the padding position
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) step<C, true>(S, in, lds, j & 1, o);
+    const int e = ring_at(head, live ? j : 0, R);
+    const uint32_t er = (uint32_t)e * (uint32_t)HD;   // ring entry, elements
     const uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
-    so.bf16<4>(out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
-    sv.bf16<4>(out_lane, (er + c0) * 2, in.vw);
-    sk.bf16<C::RPT>(key_lane, (er + r0) * 2, in.kw);
-    sa.f32<C::RPT>(key_lane, (er + r0) * 4, in.a);
+    so.bf16<4>(live && out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
+    sv.bf16<4>(live && out_lane, (er + c0) * 2, in.vw);
+    sk.bf16<C::RPT>(live && key_lane, (er + r0) * 2, in.kw);
+    sa.f32<C::RPT>(live && key_lane, (er + r0) * 4, in.a);
     const float bv[1] = {in.b};
-    sb.f32<1>(b_lane, (uint32_t)wrap(head + j, R) * (uint32_t)P.H * 4, bv);
-  }
+    sb.f32<1>(live && b_lane, (uint32_t)e * (uint32_t)P.H * 4, bv);
+  });
   if (t == 0 && h == 0 && vs == 0) {
     P.meta[slot].v_base = head;
     P.meta[slot].v_npos = n_pos;
@@ -362,25 +418,18 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, cons
   const int n = 1 + na;
   float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
   float S[C::RPT][4];
-  load_state<C>(S, Sp, r0, c0);
   auto fetch = [&](StepRaw<C>& r, int j) {
-    const size_t e = ((size_t)slot * R + (size_t)wrap(vb + j, R)) * P.H + h;
+    const size_t e = ((size_t)slot * R + (size_t)ring_at(vb, j, R)) * P.H + h;
     fetch_in<C, false>(r, nullptr, P.ring_k + e * D, P.ring_v + e * D, P.ring_a + e * D, P.ring_b + e,
                        r0, c0);
   };
-  StepRaw<C> nxt;
-  fetch(nxt, 0);
-  state_ready<C>(S);
-  for (int j = 0; j < n; ++j) {
-    StepIn<C> in;
-    unpack_in<C, false>(in, nxt);
-    if (j + 1 < n) fetch(nxt, j + 1);
+  stepped_positions<C, false>(n, S, Sp, r0, c0, fetch, [&](int j, const StepIn<C>& in) {
     float o[4];
-    step<C, false>(S, in, lds, j & 1, o);
-  }
+    if (j < n) step<C, false>(S, in, lds, j & 1, o);   // j == n: padding position
+  });
   store_state<C>(S, Sp, r0, c0);
   if (t == 0 && h == 0 && vs == 0) {
-    P.meta[slot].ring_head = wrap(vb + n, R);
+    P.meta[slot].ring_head = ring_at(vb, n, R);
     P.meta[slot].pos += n;
     P.meta[slot].pending = 0;
     if (bad) atomicOr(P.err, (uint32_t)KDA_DEVERR_NACC_RANGE);
