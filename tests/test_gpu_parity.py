@@ -162,6 +162,51 @@ def test_verify_commit_rollback_full_size():
 
 
 @pytest.mark.parametrize("d", [128, 16])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 9])
+def test_verify_commit_every_position_count(d, P):
+    """Verify of P positions (odd counts end the kernels' two-position loop with a padding
+    position, even ones do not), then commits accepting P - 1 and 0 drafts on two sequences:
+    outputs, ring entries and metadata against the oracle, nothing written by the padding
+    position, and the committed states bit-identical to the same positions applied as decode
+    calls."""
+    H, R = 4, 9
+    rng = np.random.default_rng(700 + 10 * P + d)
+    g, o = pools(8, H, d, R)
+    slots = np.array([2, 5], dtype=np.int32)
+    st = ki.draw_states(rng, 2, H, d, d)
+    put_states(g, o, slots, st)
+    tok = ki.draw_tokens(rng, (2, P), H, d, d)
+    before = g.state.clone()
+    ring_before = [t.clone() for t in g.ring_tensors()]
+    O = g.kda_verify(*tok_dev(tok), slots)
+    Oo = o.verify(tok.np, slots)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    assert torch.equal(g.state, before), "verify must not write any state"
+    ring_check(g, o, slots)
+    # ring entries past the P written ones (in ring order from the old head) are untouched
+    for t_new, t_old in zip(g.ring_tensors(), ring_before):
+        for s_ in slots:
+            assert torch.equal(t_new[int(s_)][P:], t_old[int(s_)][P:])
+    meta_equal(g.meta_array(), o.meta(), slots)
+    na = np.array([P - 1, 0], dtype=np.int32)
+    g.kda_commit(slots, torch.from_numpy(na).to("cuda"))
+    o.commit(slots, na)
+    torch.cuda.synchronize()
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+    g2, _ = pools(8, H, d, R)
+    g2.state.copy_(before)
+    for j in range(P):
+        live = [i for i in range(2) if j <= na[i]]
+        tj = [dev(x[live, j]) for x in (tok.q, tok.k, tok.v, tok.a, tok.b)]
+        g2.kda_decode(*tj, slots[live])
+    torch.cuda.synchronize()
+    assert torch.equal(g2.state[slots.tolist()], g.state[slots.tolist()])
+    assert g.kda_read_device_error() == 0
+
+
+@pytest.mark.parametrize("d", [128, 16])
 def test_direct_per_draft_checkpoints_match_ring_scheme(d):
     """Direct per-draft state checkpoints beside ReplaySSM: the same outputs as the ring
     verify (bit for bit), draft states equal to the oracle's prefix states, and a direct
