@@ -340,21 +340,55 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void decode_kernel(PoolView P, Step
   if (t == 0 && h == 0 && vs == 0) P.meta[slot].pos += 1;
 }
 
-// Speculative verify: n_pos positions on a register copy; outputs + ring appends only.
+// The ring append of a verify: the entries are the verify's own inputs (k, v, a, b of each
+// position), so extra work-groups of the same launch, one per (sequence, head), copy them while
+// the stepping work-groups run; the loop over positions then stores only its outputs (the five
+// masked ring stores per position cost ~1.7 us of that loop at 4 sequences). Entry j of the head
+// goes to ring entry ring_at(head, j, R), as the replay at commit reads it.
+template <int D>
+__device__ __forceinline__ void ring_append(const PoolView& P, const StepTensors& T, int n_pos, int bi, int h,
+                                            int slot, int head) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  constexpr int CPP = D / 2;                       // 16-byte pieces per position: k D/8, v D/8, a D/4
+  const int t = threadIdx.x, R = P.R, total = n_pos * CPP;
+  for (int x = t; x < total; x += blockDim.x) {
+    const int j = x / CPP, u = x % CPP;
+    const size_t src = ((size_t)bi * n_pos + j) * P.H + h, dst = ((size_t)slot * R + ring_at(head, j, R)) * P.H + h;
+    if (u < D / 8)
+      reinterpret_cast<u4*>(P.ring_k + dst * D)[u] = reinterpret_cast<const u4*>(T.k + src * D)[u];
+    else if (u < D / 4)
+      reinterpret_cast<u4*>(P.ring_v + dst * D)[u - D / 8] = reinterpret_cast<const u4*>(T.v + src * D)[u - D / 8];
+    else
+      reinterpret_cast<u4*>(P.ring_a + dst * D)[u - D / 4] = reinterpret_cast<const u4*>(T.a + src * D)[u - D / 4];
+  }
+  for (int j = t; j < n_pos; j += blockDim.x)
+    P.ring_b[((size_t)slot * R + ring_at(head, j, R)) * P.H + h] = T.b[((size_t)bi * n_pos + j) * P.H + h];
+}
+
+// Speculative verify: n_pos positions on a register copy; outputs + ring appends only. Grid:
+// B * H * (D / VS) stepping work-groups, then B * H ring-append work-groups.
 template <int D>
 __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, StepTensors T, int n_pos,
                                                                 const int32_t* __restrict__ slots) {
   using C = StepCfg<D>;
   __shared__ StepLds<C> lds;
   constexpr int NVS = D / C::VS;
+  const int n_step = gridDim.x / (NVS + 1) * NVS;   // stepping work-groups; the rest append
+  if ((int)blockIdx.x >= n_step) {
+    const int hb = blockIdx.x - n_step, h = hb % P.H, bi = hb / P.H;
+    const int slot = slots[bi];
+    if (slot < 0 || slot >= P.num_slots) return;     // flagged by the stepping work-groups
+    ring_append<D>(P, T, n_pos, bi, h, slot, wrap(P.meta[slot].ring_head, P.R));
+    return;
+  }
   const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
   const int slot = slots[bi];
   if (slot < 0 || slot >= P.num_slots) {
     if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
     return;
   }
-  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
-  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
+  const int t = threadIdx.x, rg = t / C::TPR;
+  const int r0 = rg * C::RPT, c0 = vs * C::VS + (t % C::TPR) * 4;
   const int R = P.R;
   const int head = wrap(P.meta[slot].ring_head, R);
   const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D;
@@ -363,28 +397,17 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
     const size_t row = ((size_t)bi * n_pos + j) * P.H + h;
     fetch_in<C, true>(r, T.q + row * D, T.k + row * D, T.v + row * D, T.a + row * D, T.b + row, r0, c0);
   };
-  // outputs of this sequence and head (rows j of n_pos), and the slot's ring for this head
-  // (entries wrap(head + j, R) of R): byte ranges small enough for 32-bit buffer offsets
+  // outputs of this sequence and head (rows j of n_pos): a byte range small enough for 32-bit
+  // buffer offsets
   const size_t HD = (size_t)P.H * D;
   const MaskedStore so(T.o + ((size_t)bi * n_pos * P.H + h) * D, (uint32_t)(n_pos * HD * 2));
-  const size_t ring0 = ((size_t)slot * R * P.H + h) * D;
-  const MaskedStore sk(P.ring_k + ring0, (uint32_t)(R * HD * 2)), sv(P.ring_v + ring0, (uint32_t)(R * HD * 2));
-  const MaskedStore sa(P.ring_a + ring0, (uint32_t)(R * HD * 4));
-  const MaskedStore sb(P.ring_b + (size_t)slot * R * P.H + h, (uint32_t)(R * P.H * 4));
-  const bool out_lane = rg == 0, key_lane = vs == 0 && cg == 0, b_lane = key_lane && t == 0;
+  const bool out_lane = rg == 0;
   stepped_positions<C, true>(n_pos, S, Sp, r0, c0, fetch, [&](int j, const StepIn<C>& in) {
     const bool live = j < n_pos;   // false only at the padding position
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     if (live) step<C, true>(S, in, lds, j & 1, o);
-    const int e = ring_at(head, live ? j : 0, R);
-    const uint32_t er = (uint32_t)e * (uint32_t)HD;   // ring entry, elements
     const uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
     so.bf16<4>(live && out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
-    sv.bf16<4>(live && out_lane, (er + c0) * 2, in.vw);
-    sk.bf16<C::RPT>(live && key_lane, (er + r0) * 2, in.kw);
-    sa.f32<C::RPT>(live && key_lane, (er + r0) * 4, in.a);
-    const float bv[1] = {in.b};
-    sb.f32<1>(live && b_lane, (uint32_t)e * (uint32_t)P.H * 4, bv);
   });
   if (t == 0 && h == 0 && vs == 0) {
     P.meta[slot].v_base = head;
@@ -631,9 +654,11 @@ hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, con
 hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
                          const int32_t* d_slots, hipStream_t s) {
   if (p.dk == 128)
-    hipLaunchKernelGGL(verify_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, t, n_pos, d_slots);
+    hipLaunchKernelGGL(verify_kernel<128>, dim3(step_blocks<128>(p, B) + B * p.H), dim3(StepCfg<128>::NT), 0, s, p,
+                       t, n_pos, d_slots);
   else
-    hipLaunchKernelGGL(verify_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, t, n_pos, d_slots);
+    hipLaunchKernelGGL(verify_kernel<16>, dim3(step_blocks<16>(p, B) + B * p.H), dim3(StepCfg<16>::NT), 0, s, p, t,
+                       n_pos, d_slots);
   return hipGetLastError();
 }
 
