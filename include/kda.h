@@ -222,10 +222,10 @@ kda_status kda_commit_direct(kda_pool* pool, int32_t B, const int32_t* h_slots,
  * and the step slot arrays of `prefill`, `decode` and `verify` are ignored in favour of the
  * packed ones below. Commit, decode and verify touch only their own slots, so when the batch
  * also has a prefill they run (in that order) on a side stream owned by the pool (default priority, created on
- * first use, destroyed by kda_pool_destroy) while the prefill's sequential pass runs on
- * `stream`: forked by an event recorded on `stream` after the prefill's first kernels,
- * joined by an event that `stream` waits on before the call returns. Everything enqueued on
- * `stream` afterwards is ordered after all three parts.                                  */
+ * first use, destroyed by kda_pool_destroy) while the prefill's kernels run on `stream`:
+ * forked by an event recorded on `stream` before the prefill's first kernel, joined by an
+ * event that `stream` waits on before the call returns. Everything enqueued on `stream`
+ * afterwards is ordered after all three parts.                                           */
 typedef struct {
   const void* q; const void* k; const void* v;   /* bf16 [n_total][H][d] */
   const float* a; const float* b;

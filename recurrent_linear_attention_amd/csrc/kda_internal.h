@@ -67,22 +67,12 @@ hipError_t launch_commit_direct(const PoolView& p, int32_t B, const int32_t* d_s
 hipError_t launch_slot_reset(const PoolView& p, int32_t slot, hipStream_t s);
 hipError_t launch_slot_copy(const PoolView& p, int32_t src, int32_t dst, hipStream_t s);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t s);
-// Called by launch_prefill once the S-independent part is enqueued and before the sequential
-// part: lets the caller start independent work that overlaps the latter.
-struct PrefillHook {
-  hipError_t (*fn)(void* ctx);
-  void* ctx;
-};
-hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s,
-                          const PrefillHook* after_prep = nullptr);
+hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
 // Width plan for the sequential pass of a prefill with host lengths h_cu[0..n_seq]. Long
 // chains take narrow slices (a chunk's latency falls with fewer compute waves sharing a CU's
 // LDS), short ones wide slices (fewer work-groups, each CU-cheaper per column), chosen by a
-// latency / CU-time model of the pass; beyond 64 sequences, and with shared (independent work
-// runs next to the pass, as in a mixed batch), one width for all: there the other work needs the
-// CUs that the short chains free, and the long chains slow under its HBM traffic, which the
-// model leaves out.
-StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H, bool shared);
+// latency / CU-time model of the pass; beyond 64 sequences one width for all.
+StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H);
 // Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
 // shapes that run the token-by-token kernel).
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);

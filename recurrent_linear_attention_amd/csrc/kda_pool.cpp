@@ -241,7 +241,7 @@ kda_status kda_slot_free(kda_pool* p, int32_t s) {
 int32_t kda_prefill_plan(const kda_pool* p, int32_t n_seq, const int32_t* h_cu, int32_t* rank_end,
                          int32_t* vsw) {
   if (!p || !h_cu || !rank_end || !vsw || n_seq <= 0) return 0;
-  const kda::StatePlan sp = kda::plan_state_pass(h_cu, n_seq, p->desc.num_heads, false);
+  const kda::StatePlan sp = kda::plan_state_pass(h_cu, n_seq, p->desc.num_heads);
   for (int32_t g = 0; g < sp.n_groups; ++g) {
     rank_end[g] = sp.rank_end[g];
     vsw[g] = sp.vsw[g];
@@ -388,7 +388,7 @@ kda_status kda_prefill(kda_pool* p, const kda_prefill_args* a, void* stream) {
   kda::PrefillLaunch L{tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->n_seq, a->n_tok,
                        a->chunk, a->ckpt_interval, a->d_cu_seqlens, a->d_init_slot,
                        a->d_out_slot, a->d_ckpt_slot, max_len, n_chunks, ws};
-  L.plan = kda::plan_state_pass(a->h_cu_seqlens, a->n_seq, p->desc.num_heads, false);
+  L.plan = kda::plan_state_pass(a->h_cu_seqlens, a->n_seq, p->desc.num_heads);
   hipError_t e = kda::launch_prefill(p->view, L, as_stream(stream));
   return e == hipSuccess ? KDA_OK : hip_fail(e, "prefill launch");
 }
@@ -507,8 +507,10 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   };
   // Commit, decode and verify touch only their own slots (checked distinct from the
   // prefill's above), so they need no order against the prefill: with a prefill in the batch
-  // they go to the side stream, in that order, once the prefill's S-independent kernel is
-  // enqueued, and the caller's stream waits for them before anything later.
+  // they go to the side stream, in that order, ahead of the prefill's kernels, and the caller's
+  // stream waits for them before anything later. They then run beside the prefill's
+  // S-independent kernel (whose work-groups leave room on each CU) and are done before its
+  // sequential pass starts, which therefore keeps every CU and its width plan.
   struct StepLaunches {
     kda_pool* p;
     const kda_mixed_args* m;
@@ -529,12 +531,11 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
         e = kda::launch_verify(p->view, ver, m->n_verify, m->n_pos, m->d_verify_slots, on);
       return e;
     }
-    static hipError_t forked(void* ctx) {
-      const StepLaunches* sl = static_cast<const StepLaunches*>(ctx);
-      hipError_t e = hipEventRecord(sl->p->ev_fork, sl->s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(sl->p->aux, sl->p->ev_fork, 0);
-      if (e == hipSuccess) e = sl->run(sl->p->aux);
-      if (e == hipSuccess) e = hipEventRecord(sl->p->ev_join, sl->p->aux);
+    hipError_t forked() const {
+      hipError_t e = hipEventRecord(p->ev_fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_fork, 0);
+      if (e == hipSuccess) e = run(p->aux);
+      if (e == hipSuccess) e = hipEventRecord(p->ev_join, p->aux);
       return e;
     }
   };
@@ -554,9 +555,12 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     kda::PrefillLaunch L{part(0), pre.n_seq, pre.n_tok, pre.chunk, pre.ckpt_interval,
                          pre.d_cu_seqlens, pre.d_init_slot, pre.d_out_slot, pre.d_ckpt_slot,
                          max_len, n_chunks, ws};
-    L.plan = kda::plan_state_pass(pre.h_cu_seqlens, pre.n_seq, H, sl.fork);
-    const kda::PrefillHook hook{&StepLaunches::forked, &sl};
-    e = kda::launch_prefill(p->view, L, s, sl.fork ? &hook : nullptr);
+    L.plan = kda::plan_state_pass(pre.h_cu_seqlens, pre.n_seq, H);
+    if (sl.fork) {
+      e = sl.forked();
+      if (e != hipSuccess) return hip_fail(e, "mixed: side stream");
+    }
+    e = kda::launch_prefill(p->view, L, s);
     if (e != hipSuccess) return hip_fail(e, "mixed: prefill launch");
     if (sl.fork) {
       e = hipStreamWaitEvent(s, p->ev_join, 0);

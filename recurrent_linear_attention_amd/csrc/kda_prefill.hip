@@ -985,15 +985,8 @@ size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_ch
   return plan_bytes(n_seq) + (size_t)n_chunks * H * BLOCK_BYTES;
 }
 
-hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s,
-                          const PrefillHook* after_prep) {
-  if (p.dk != PD || a.chunk != PC) {
-    if (after_prep) {
-      const hipError_t e = after_prep->fn(after_prep->ctx);
-      if (e != hipSuccess) return e;
-    }
-    return launch_prefill_recurrent(p, a, s);
-  }
+hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
+  if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
   if (a.n_seq <= 0) return hipSuccess;
   char* ws = static_cast<char*>(a.workspace);
   int32_t* choff = reinterpret_cast<int32_t*>(ws);
@@ -1013,14 +1006,10 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (after_prep) {
-    e = after_prep->fn(after_prep->ctx);
-    if (e != hipSuccess) return e;
-  }
   return launch_state(p, a, choff, ckoff, order, blocks, s);
 }
 
-StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H, bool shared) {
+StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H) {
   // Per-chunk latency of one chain (us) with 16, 32, 64 and 128 value columns per work-group,
   // measured on MI355X for the mixed 16384-token batch, plus a work-group's start-up; the pass
   // keeps one work-group per CU, and list scheduling in rank order packs CU-time to ~85%.
@@ -1047,7 +1036,7 @@ StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H, bool shared) {
   const int wu = n_hg * 8 <= cus ? 0 : (n_hg * 4 <= cus ? 1 : 2);
   const int end_all[1] = {n_seq}, w_all[1] = {WIDTH[wu]};
   const StatePlan uniform = build(1, end_all, w_all);
-  if (shared || n_seq < 2 || n_seq > PLAN_INLINE_MAX) return uniform;
+  if (n_seq < 2 || n_seq > PLAN_INLINE_MAX) return uniform;
   // chunk counts in rank order: descending length, ties lower index first (the plan's order)
   int idx[PLAN_INLINE_MAX], nch[PLAN_INLINE_MAX];
   for (int i = 0; i < n_seq; ++i) idx[i] = i;
