@@ -47,9 +47,9 @@ RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
 # bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid only for the kernel source it was
 # measured on (first 16 hex digits of its SHA-256); for any other source the bench reports
 # traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "3ba87724f491a99b", "fetch_scale": 2.0, "write_scale": 1.0,
-                   "fetch_kib": {"chunk_prep_kernel": 269327, "state_pass_kernel": 316203},
-                   "write_kib": {"chunk_prep_kernel": 501494, "state_pass_kernel": 142817}}
+PREFILL_TRAFFIC = {"source_sha256_16": "4d34be1df2b4e43e", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"chunk_prep_kernel": 269326, "state_pass_kernel": 316202},
+                   "write_kib": {"chunk_prep_kernel": 501492, "state_pass_kernel": 142817}}
 
 
 def prefill_traffic_bytes():
