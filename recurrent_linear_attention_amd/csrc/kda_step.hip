@@ -6,15 +6,17 @@
 // whole stack" -- but print no formula):
 //     S' = Diag(a) S;  u = S'^T k;  p = S'^T q;  delta = b (v - u)
 //     S  = S' + k delta^T;  o = S^T q = p + (k . q) delta
-// These kernels are HBM-bound (about 0.9 flop per byte): each (sequence, head, value-column
-// slice) work-group streams its fp32 state tile in once with 16-byte loads, keeps it in
-// VGPRs for every position it processes, and writes it back at most once.
+// Each (sequence, head, value-column slice) work-group streams its fp32 state tile in once with
+// 16-byte loads, keeps it in VGPRs for every position it processes, and writes it back at most
+// once: decode is HBM-bound (about 0.9 flop per byte); verify and commit of a few sequences are
+// bound by the chain of positions instead (one wave per SIMD stepping one position after
+// another).
 //
 // Thread layout (StepCfg): a work-group owns VS value columns of one head. Thread t holds
 // RPT consecutive key rows x 4 consecutive columns (one float4 per row). The reductions over
 // key rows (u, p and k.q) go first through the thread's own rows, then a butterfly across
-// the lanes of a wave that hold the same columns, then across waves through LDS in wave
-// order. Decode, verify and commit use the same layout and the same step function, so a
+// the lanes of a wave that hold the same columns (DPP and lane-swap instructions), then across
+// waves through LDS in wave order. Decode, verify and commit use the same layout and the same step function, so a
 // commit that replays n positions yields the state bit-for-bit equal to n decode calls.
 #include <hip/hip_runtime.h>
 
@@ -223,48 +225,20 @@ __device__ __forceinline__ int ring_at(int base, int j, int R) {
 }
 
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-// Stores through a buffer resource over [base, base + bytes) whose lanes opt out with an
-// offset past the range (the hardware drops them): every wave issues the same store
+// 8-byte stores through a buffer resource over [base, base + bytes) whose lanes opt out with
+// an offset past the range (the hardware drops them): every wave issues the same store
 // instructions whatever its lanes' roles, so a loop that prefetches its next position's inputs
-// before these stores waits only for those loads (a fixed count of later operations), not
-// for the stores to retire.
+// before these stores waits only for those loads (a fixed count of later operations), not for
+// the stores to retire.
 struct MaskedStore {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t oob;
   __device__ __forceinline__ MaskedStore(const void* base, uint32_t bytes)
       : rs(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)),
         oob(bytes) {}
-  __device__ __forceinline__ uint32_t at(bool on, uint32_t byte_off) const { return on ? byte_off : oob; }
-  template <int N>   // N raw bf16 words (N = 1, 4 or 8)
-  __device__ __forceinline__ void bf16(bool on, uint32_t off, const uint32_t (&w)[(N + 1) / 2]) const {
-    const uint32_t o = at(on, off);
-    if constexpr (N == 1) {
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[0], rs, o, 0, 0);
-    } else if constexpr (N == 4) {
-      __builtin_amdgcn_raw_buffer_store_b64(u2v{w[0], w[1]}, rs, o, 0, 0);
-    } else {
-      static_assert(N % 8 == 0, "bf16 vector width");
-#pragma unroll
-      for (int i = 0; i < N / 8; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(u4v{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]}, rs,
-                                               at(on, off + 16 * i), 0, 0);
-    }
-  }
-  template <int N>   // N floats (N = 1 or a multiple of 4)
-  __device__ __forceinline__ void f32(bool on, uint32_t off, const float (&f)[N]) const {
-    if constexpr (N == 1) {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f[0]), rs, at(on, off), 0, 0);
-    } else {
-      static_assert(N % 4 == 0, "float vector width");
-#pragma unroll
-      for (int i = 0; i < N / 4; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u4v{__float_as_uint(f[4 * i]), __float_as_uint(f[4 * i + 1]), __float_as_uint(f[4 * i + 2]),
-                __float_as_uint(f[4 * i + 3])},
-            rs, at(on, off + 16 * i), 0, 0);
-    }
+  __device__ __forceinline__ void b64(bool on, uint32_t byte_off, const uint32_t (&w)[2]) const {
+    __builtin_amdgcn_raw_buffer_store_b64(u2v{w[0], w[1]}, rs, on ? byte_off : oob, 0, 0);
   }
 };
 
@@ -407,7 +381,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     if (live) step<C, true>(S, in, lds, j & 1, o);
     const uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
-    so.bf16<4>(live && out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
+    so.b64(live && out_lane, (uint32_t)((size_t)j * HD + c0) * 2, ow);
   });
   if (t == 0 && h == 0 && vs == 0) {
     P.meta[slot].v_base = head;
