@@ -12,16 +12,8 @@ constexpr uint32_t DEVERR_SLOT_RANGE = KDA_DEVERR_SLOT_RANGE;
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Two fp32 values -> packed bf16 (lo in bits 0-15), round to nearest even: one
-// v_cvt_pk_bf16_f32 on gfx950 (equal to f2bf for every non-NaN input).
+// Two fp32 values -> packed bf16 (lo in bits 0-15), round to nearest even (NaN stays NaN): one
+// v_cvt_pk_bf16_f32 on gfx950.
 typedef __bf16 kda_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float kda_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
