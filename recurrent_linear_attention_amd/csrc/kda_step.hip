@@ -15,9 +15,10 @@
 // Thread layout (StepCfg): a work-group owns VS value columns of one head. Thread t holds
 // RPT consecutive key rows x 4 consecutive columns (one float4 per row). The reductions over
 // key rows (u, p and k.q) go first through the thread's own rows, then a butterfly across
-// the lanes of a wave that hold the same columns (DPP and lane-swap instructions), then across
-// waves through LDS in wave order. Decode, verify and commit use the same layout and the same step function, so a
-// commit that replays n positions yields the state bit-for-bit equal to n decode calls.
+// the lanes of a wave that hold the same columns (DPP and lane-swap instructions), then
+// across waves through LDS in wave order. Decode, verify and commit use the same layout and
+// the same step function, so a commit that replays n positions yields the state bit-for-bit
+// equal to n decode calls.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
