@@ -207,6 +207,106 @@ def test_verify_commit_every_position_count(d, P):
 
 
 @pytest.mark.parametrize("d", [128, 16])
+def test_verify_commit_at_ring_capacity(d):
+    """The largest ring a pool takes (64 entries): verify of 64 positions, commits accepting 63
+    and 0 drafts, against the oracle; the committed states bit-identical to the same positions
+    applied as decode calls."""
+    H, R, P = 2, 64, 64
+    rng = np.random.default_rng(900 + d)
+    g, o = pools(6, H, d, R)
+    slots = np.array([1, 4], dtype=np.int32)
+    put_states(g, o, slots, ki.draw_states(rng, 2, H, d, d))
+    tok = ki.draw_tokens(rng, (2, P), H, d, d)
+    before = g.state.clone()
+    O = g.kda_verify(*tok_dev(tok), slots)
+    Oo = o.verify(tok.np, slots)
+    torch.cuda.synchronize()
+    assert rel_bf16(O, Oo) <= TOL
+    assert torch.equal(g.state, before)
+    ring_check(g, o, slots)
+    na = np.array([P - 1, 0], dtype=np.int32)
+    g.kda_commit(slots, torch.from_numpy(na).to("cuda"))
+    o.commit(slots, na)
+    torch.cuda.synchronize()
+    assert rel(g.state[slots.tolist()], o.state[slots]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), slots)
+    g2, _ = pools(6, H, d, R)
+    g2.state.copy_(before)
+    for j in range(P):
+        live = [i for i in range(2) if j <= na[i]]
+        tj = [dev(x[live, j]) for x in (tok.q, tok.k, tok.v, tok.a, tok.b)]
+        g2.kda_decode(*tj, slots[live])
+    torch.cuda.synchronize()
+    assert torch.equal(g2.state[slots.tolist()], g.state[slots.tolist()])
+    assert g.kda_read_device_error() == 0
+
+
+def test_rule_invariants_at_full_size():
+    """Properties of the rule checked on the device at the decode workload's size (16 sequences,
+    32 heads, d = 128), independent of the oracle: with b = 0 and a = 1 nothing is written --
+    decode, verify + full commit and a resumed prefill leave the state bit-identical; with a = 1,
+    b = 1 and a one-hot key e_i, row i of the new state is the value vector."""
+    w = ki.decode_workload(1)
+    H, d = w["H"], w["dk"]
+    g, _ = pools(w["n_slots"], H, d)
+    slots = w["slots"]
+    g.state[slots.tolist()] = w["states"].to("cuda")
+    rng = np.random.default_rng(950)
+    B = len(slots)
+    # no write: b = 0, a = 1
+    tok = ki.draw_tokens(rng, (B,), H, d, d)
+    tok.a.fill_(1.0)
+    tok.b.zero_()
+    before = g.state.clone()
+    g.kda_decode(*tok_dev(tok), slots)
+    vt = ki.draw_tokens(rng, (B, 9), H, d, d)
+    vt.a.fill_(1.0)
+    vt.b.zero_()
+    g.kda_verify(*tok_dev(vt), slots)
+    g.kda_commit(slots, torch.full((B,), 8, dtype=torch.int32, device="cuda"))
+    pt = ki.draw_tokens(rng, (300,), H, d, d)
+    pt.a.fill_(1.0)
+    pt.b.zero_()
+    free = [s_ for s_ in range(w["n_slots"]) if s_ not in set(slots.tolist())][:1]
+    g.kda_prefill(*tok_dev(pt), [0, 300], free, init_slots=[int(slots[0])])
+    torch.cuda.synchronize()
+    assert torch.equal(g.state[slots.tolist()], before[slots.tolist()])
+    assert torch.equal(g.state[free[0]], before[int(slots[0])])
+    # unit-key readout: a = 1, b = 1, k = e_i  =>  S_new[i, :] = v
+    tok = ki.draw_tokens(rng, (B,), H, d, d)
+    tok.a.fill_(1.0)
+    tok.b.fill_(1.0)
+    idx = rng.integers(0, d, size=(B, H))
+    k = torch.zeros((B, H, d), dtype=torch.bfloat16)
+    k[np.arange(B)[:, None], np.arange(H)[None, :], idx] = 1.0
+    tok.k = k
+    g.kda_decode(*tok_dev(tok), slots)
+    torch.cuda.synchronize()
+    ib = torch.arange(B, device="cuda")[:, None]
+    ih = torch.arange(H, device="cuda")[None, :]
+    rows = g.state[slots.tolist()][ib, ih, torch.from_numpy(idx).to("cuda")]
+    v = tok.v.float().to("cuda")
+    scale = torch.maximum(v.abs().max(), g.state[slots.tolist()].abs().max())
+    assert ((rows - v).abs().max() / scale).item() <= 1e-6
+    assert g.kda_read_device_error() == 0
+
+
+def test_prefill_flags_a_decay_out_of_range():
+    """A key channel that decays by more than 2^-14 within 16 tokens (a = 0.3 there) is flagged
+    with KDA_DEVERR_DECAY_RANGE (the prefill's fp16 operands of that block lose accuracy);
+    reading the error word clears it."""
+    H, d = 2, 128
+    g, _ = pools(4, H, d)
+    rng = np.random.default_rng(960)
+    tok = ki.draw_tokens(rng, (128,), H, d, d)
+    tok.a[:, 1, 5] = 0.3
+    g.kda_prefill(*tok_dev(tok), [0, 128], [0])
+    torch.cuda.synchronize()
+    assert g.kda_read_device_error() & kda._abi.KDA_DEVERR_DECAY_RANGE
+    assert g.kda_read_device_error() == 0
+
+
+@pytest.mark.parametrize("d", [128, 16])
 def test_direct_per_draft_checkpoints_match_ring_scheme(d):
     """Direct per-draft state checkpoints beside ReplaySSM: the same outputs as the ring
     verify (bit for bit), draft states equal to the oracle's prefix states, and a direct
