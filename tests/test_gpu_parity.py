@@ -834,6 +834,46 @@ def test_mixed_batch_full_size_sampled():
 
 
 
+def test_mixed_batch_decode_heavy():
+    """A mixed batch whose side-stream work (a commit, 64 decodes and 8 verifies of 1+8)
+    outlasts its short prefill's operand kernel, so the state pass runs beside it: every part
+    against the oracle, all heads."""
+    rng = np.random.default_rng(321)
+    H, d, P = 4, 128, 9
+    lengths = [65, 1]
+    n_dec, n_ver = 64, 8
+    n_slots = 2 + n_dec + n_ver
+    g, o = pools(n_slots, H, d, R=P)
+    ps = np.arange(2)
+    ds = np.arange(2, 2 + n_dec)
+    vs = np.arange(2 + n_dec, n_slots)
+    put_states(g, o, np.concatenate([ds, vs]), ki.draw_states(rng, n_dec + n_ver, H, d, d))
+    # a first verify on vs, committed by the batch below ahead of its own verify
+    t0 = ki.draw_tokens(rng, (n_ver, P), H, d, d)
+    g.kda_verify(*tok_dev(t0), vs)
+    o.verify(t0.np, vs)
+    na = rng.integers(0, P, size=n_ver).astype(np.int32)
+    o.commit(vs, na)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    n_pre = int(cu[-1])
+    tok = ki.draw_tokens(rng, (n_pre + n_dec + n_ver * P,), H, d, d)
+    O = g.kda_mixed_batch(*tok_dev(tok), cu, ps, ds, vs, P, commit_slots=vs,
+                          n_accepted=torch.from_numpy(na).to("cuda"))
+    Op = o.prefill(tok.slice(0, n_pre).np, cu, [-1, -1], ps, [], 0)
+    Od = o.decode(tok.slice(n_pre, n_pre + n_dec).np, ds)
+    vt = {k_: x[n_pre + n_dec:].reshape((n_ver, P) + x.shape[1:]) for k_, x in tok.np.items()}
+    Ov = o.verify(vt, vs)
+    torch.cuda.synchronize()
+    assert rel_bf16(O[:n_pre], Op) <= TOL
+    assert rel_bf16(O[n_pre:n_pre + n_dec], Od) <= TOL
+    assert rel_bf16(O[n_pre + n_dec:].reshape(n_ver, P, H, d), Ov) <= TOL
+    for s_ in np.concatenate([ps, ds, vs]):
+        assert rel(g.state[int(s_)], o.state[s_]) <= TOL, s_
+    meta_equal(g.meta_array(), o.meta(), np.arange(n_slots))
+    ring_check(g, o, vs)
+    assert g.kda_read_device_error() == 0
+
+
 def test_mixed_batch_many_prefills():
     """A mixed batch with 70 prompts (more than the operand kernel plans itself: the plan
     kernel runs on the caller's stream) next to decodes and a verify on the side stream:
