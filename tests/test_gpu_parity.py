@@ -906,12 +906,13 @@ def test_mixed_batch_many_prefills():
     ring_check(g, o, vs)
     assert g.kda_read_device_error() == 0
 
-def test_mixed_batch_commits_previous_verify():
+@pytest.mark.parametrize("d", [128, 16])
+def test_mixed_batch_commits_previous_verify(d):
     """Two serving steps: the second mixed batch commits the first one's verified drafts (its
     commit part) before verifying the same slots again, next to a new prefill and decodes.
     Every output, state and metadata entry against the oracle applying the same operations in
-    order."""
-    H, d, P = 4, 128, 5
+    order. At d = 16 the prefill part is the token-recurrent kernel (chunk 16)."""
+    H, P = 4, 5
     g, o = pools(32, H, d)
     rng = np.random.default_rng(90)
     ds, vs = np.array([3, 7, 11], np.int32), np.array([5, 20], np.int32)
