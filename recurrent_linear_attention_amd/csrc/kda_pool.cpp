@@ -484,18 +484,21 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   if (st != KDA_OK) return st;
   if (m->n_commit > 0 && (!m->d_commit_slots || !m->d_n_accepted))
     return fail(KDA_EINVAL, "null device commit array");
+  if ((m->n_decode > 0 && !m->d_decode_slots) || (m->n_verify > 0 && !m->d_verify_slots))
+    return fail(KDA_EINVAL, "null device slot array");
   // Decode and verify slots: idle once the commits are done (they run first, in order on the
-  // same stream), distinct from each other and from the prefill's slots.
+  // same stream), distinct from each other and from the prefill's slots. The commit slots are
+  // marked idle here; every failure before the first launch marks them pending again, so a
+  // rejected call leaves the pool as it was.
   for (int32_t i = 0; i < m->n_commit; ++i) p->slot_state[m->h_commit_slots[i]] = SLOT_IDLE;
+  auto keep_pending = [&](kda_status why) {
+    for (int32_t i = 0; i < m->n_commit; ++i) p->slot_state[m->h_commit_slots[i]] = SLOT_PENDING;
+    return why;
+  };
   mark_prefill_slots();
   st = check_slots(p, m->n_decode, m->h_decode_slots, SLOT_IDLE, false);
   if (st == KDA_OK) st = check_slots(p, m->n_verify, m->h_verify_slots, SLOT_IDLE, false);
-  if (st != KDA_OK) {
-    for (int32_t i = 0; i < m->n_commit; ++i) p->slot_state[m->h_commit_slots[i]] = SLOT_PENDING;
-    return st;
-  }
-  if ((m->n_decode > 0 && !m->d_decode_slots) || (m->n_verify > 0 && !m->d_verify_slots))
-    return fail(KDA_EINVAL, "null device slot array");
+  if (st != KDA_OK) return keep_pending(st);
 
   hipStream_t s = as_stream(stream);
   const size_t n_pre = (size_t)pre.n_tok;
@@ -546,12 +549,12 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "mixed: side stream");
+    if (e != hipSuccess) return keep_pending(hip_fail(e, "mixed: side stream"));
   }
   if (pre.n_seq > 0) {
     void* ws = nullptr;
     st = prefill_workspace(p, &pre, n_chunks, &ws);
-    if (st != KDA_OK) return st;
+    if (st != KDA_OK) return keep_pending(st);
     kda::PrefillLaunch L{part(0), pre.n_seq, pre.n_tok, pre.chunk, pre.ckpt_interval,
                          pre.d_cu_seqlens, pre.d_init_slot, pre.d_out_slot, pre.d_ckpt_slot,
                          max_len, n_chunks, ws};

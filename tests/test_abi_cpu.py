@@ -311,3 +311,61 @@ def test_prefill_width_plan():
     z = np.zeros(4, np.int32)
     assert lib.kda_prefill_plan(p.h, 0, z.ctypes.data, z.ctypes.data, z.ctypes.data) == 0
     assert lib.kda_prefill_plan(p.h, 1, None, z.ctypes.data, z.ctypes.data) == 0
+
+
+def mixed_args(cu, out, dec=(), ver=(), n_pos=3, com=None, init=None, chunk=16):
+    m = _abi.kda_mixed_args(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    keep = []
+    m.prefill = prefill_args(cu, out, init=init, chunk=chunk)
+    keep += [cu, out, init]
+    for name, sl in (("decode", dec), ("verify", ver)):
+        arr = i32(*sl)
+        keep.append(arr)
+        setattr(m, "n_" + name, arr.size)
+        setattr(m, "h_" + name + "_slots", arr.ctypes.data if arr.size else None)
+        setattr(m, "d_" + name + "_slots", FAKE if arr.size else None)
+    m.n_pos = n_pos
+    if com is not None:
+        arr = i32(*com)
+        keep.append(arr)
+        m.n_commit, m.h_commit_slots, m.d_commit_slots, m.d_n_accepted = arr.size, arr.ctypes.data, FAKE, FAKE
+    return m, keep
+
+
+def test_mixed_batch_validation_errors_change_nothing():
+    """Every part of a mixed batch is validated before anything is launched: slots distinct
+    across the prefill (out and init slots), decode and verify parts, commit slots pending,
+    n_pos within the ring, device arrays present. A rejected call leaves every slot's host
+    state as it was."""
+    p = HostPool()
+    s = [p.alloc()[1] for _ in range(7)]
+    cu, out = i32(0, 20, 33), i32(s[0], s[1])
+    states = lambda: [lib.kda_slot_host_state(p.h, x) for x in range(8)]  # noqa: E731
+    before = states()
+    cases = [
+        (mixed_args(cu, out, dec=[s[2], s[1]]), _abi.KDA_EINVAL),            # decode = prefill out
+        (mixed_args(cu, out, ver=[s[0]]), _abi.KDA_EINVAL),                  # verify = prefill out
+        (mixed_args(cu, out, dec=[s[2]], init=i32(s[3], -1), ver=[s[3]]), _abi.KDA_EINVAL),  # = init
+        (mixed_args(cu, out, dec=[s[2]], ver=[s[2]]), _abi.KDA_EINVAL),      # decode = verify
+        (mixed_args(cu, out, dec=[s[2], s[2]]), _abi.KDA_EINVAL),            # repeated decode slot
+        (mixed_args(cu, out, ver=[s[2]], n_pos=10), _abi.KDA_EINVAL),        # n_pos > ring_cap
+        (mixed_args(cu, out, ver=[s[2]], n_pos=0), _abi.KDA_EINVAL),
+        (mixed_args(cu, out, dec=[7]), _abi.KDA_EINVAL),                     # not a live slot
+        (mixed_args(cu, out, com=[s[4]]), _abi.KDA_ESTATE),                  # commit of an idle slot
+        (mixed_args(cu, out, dec=[s[2]], chunk=64), _abi.KDA_EUNSUPPORTED),  # chunk 64 at d = 16
+        (mixed_args(i32(0, 20, 10), out, dec=[s[2]]), _abi.KDA_EINVAL),      # cu_seqlens decreasing
+    ]
+    for i, ((m, _keep), want) in enumerate(cases):
+        assert lib.kda_mixed_batch(p.h, byref(m), None) == want, (i, lib.kda_last_error())
+        assert states() == before, i
+    m, _keep = mixed_args(cu, out, dec=[s[2]])
+    m.d_decode_slots = None
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    m, _keep = mixed_args(cu, out, ver=[s[2]])
+    m.d_verify_slots = None
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    assert b"null device slot array" in lib.kda_last_error()
+    m, _keep = mixed_args(cu, out, dec=[s[2]])
+    m.n_decode = -1
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    assert states() == before

@@ -947,6 +947,40 @@ def test_mixed_batch_commits_previous_verify(d):
     assert g.kda_read_device_error() == 0
 
 
+def test_mixed_batch_rejected_keeps_commit_pending():
+    """A mixed batch rejected after its commit part passed validation (a decode slot that is
+    also a prefill out slot) launches nothing: the commit slots stay pending, no state or ring
+    entry changes, and the commit then runs as usual."""
+    H, d, P = 4, 128, 3
+    g, o = pools(8, H, d)
+    rng = np.random.default_rng(77)
+    vs = np.array([5, 6], dtype=np.int32)
+    put_states(g, o, vs, ki.draw_states(rng, 2, H, d, d))
+    vt = ki.draw_tokens(rng, (2, P), H, d, d)
+    g.kda_verify(*tok_dev(vt), vs)
+    o.verify(vt.np, vs)
+    torch.cuda.synchronize()
+    tok = ki.draw_tokens(rng, (21,), H, d, d)
+    na = np.array([1, 2], dtype=np.int32)
+    na_dev = torch.from_numpy(na).to("cuda")
+    before = g.state.clone()
+    ring_before = [t.clone() for t in g.ring_tensors()]
+    meta_before = g.meta_array().copy()
+    with pytest.raises(kda.KDAError):
+        g.kda_mixed_batch(*tok_dev(tok), [0, 20], [1], [1], [], P, commit_slots=vs, n_accepted=na_dev)
+    torch.cuda.synchronize()
+    assert all(g.host_state(int(s_)) == 2 for s_ in vs)
+    assert torch.equal(g.state, before)
+    assert all(torch.equal(a, b) for a, b in zip(g.ring_tensors(), ring_before))
+    assert np.array_equal(g.meta_array(), meta_before)
+    g.kda_commit(vs, na_dev)
+    o.commit(vs, na)
+    torch.cuda.synchronize()
+    assert rel(g.state[vs.tolist()], o.state[vs]) <= TOL
+    meta_equal(g.meta_array(), o.meta(), vs)
+    assert g.kda_read_device_error() == 0
+
+
 # ----------------------------------------------------------------------------- slot ops
 
 def test_slot_reset_and_checkpoint_copy():
