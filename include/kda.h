@@ -12,15 +12,21 @@
  *     o_t = S_t^T q_t
  *
  * Conventions shared by every entry point:
- *   - Tensor arguments are DEVICE pointers owned by the caller. The library never allocates
- *     or frees device memory and never synchronises, except kda_read_device_error.
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library allocates and
+ *     frees no device memory and synchronises only in kda_read_device_error, with two per-pool
+ *     exceptions documented at kda_prefill_args and kda_mixed_batch: the fallback prefill
+ *     workspace (when the caller passes none; grown after a device synchronise) and the side
+ *     stream and events of kda_mixed_batch.
  *   - Token tensors are dense row-major: q, k [n][H][dk] bf16; v [n][H][dv] bf16;
  *     a [n][H][dk] fp32 (decay in (0,1)); b [n][H] fp32; o [n][H][dv] bf16.
  *     Device pointers must be 16-byte aligned.
  *   - Slot state is fp32 [num_slots][H][dk][dv] (row = key channel, column = value channel).
- *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it only.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it only, apart
+ *     from the part of a mixed batch forked to its side stream and joined back to `stream`.
  *   - Every call returns a kda_status; kda_last_error() gives a message for the last failure
- *     on the calling thread. A failing call enqueues no device work and changes no host state.
+ *     on the calling thread. A call rejected by its checks (any status but KDA_EHIP) enqueues
+ *     no device work and changes no host state. KDA_EHIP means a HIP runtime call failed; part
+ *     of the call's work may have been enqueued by then.
  *   - One pool is driven from one host thread at a time.
  *   - Supported shapes: dk == dv in {16, 128}; prefill chunk 16 (dk 16) or 64 (dk 128).
  */
