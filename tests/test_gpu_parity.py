@@ -947,6 +947,31 @@ def test_mixed_batch_commits_previous_verify(d):
     assert g.kda_read_device_error() == 0
 
 
+def test_mixed_batch_is_deterministic():
+    """The same mixed batch (prefill on the caller's stream, commit / decode / verify on the
+    side stream) on two pools with the same contents gives the same bytes: outputs, states,
+    ring entries and metadata."""
+    H, d, P = 4, 128, 5
+    rng = np.random.default_rng(31)
+    ds, vs = [3, 4, 9], [6, 7]
+    st = ki.draw_states(rng, 5, H, d, d)
+    lens = [300, 129, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]) + len(ds) + len(vs) * P,), H, d, d)
+    res = []
+    for _ in range(2):
+        g, o = pools(12, H, d)
+        put_states(g, o, ds + vs, st)
+        O = g.kda_mixed_batch(*tok_dev(tok), cu, [0, 1, 2], ds, vs, P)
+        torch.cuda.synchronize()
+        res.append((O.clone(), g.state.clone(), [t.clone() for t in g.ring_tensors()], g.meta_array()))
+    (O1, S1, R1, M1), (O2, S2, R2, M2) = res
+    assert torch.equal(O1, O2)
+    assert torch.equal(S1, S2)
+    assert all(torch.equal(a, b) for a, b in zip(R1, R2))
+    assert np.array_equal(M1, M2)
+
+
 def test_mixed_batch_rejected_keeps_commit_pending():
     """A mixed batch rejected after its commit part passed validation (a decode slot that is
     also a prefill out slot) launches nothing: the commit slots stay pending, no state or ring
