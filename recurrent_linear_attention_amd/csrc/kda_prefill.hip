@@ -30,8 +30,11 @@
 //     2e-3 of the sequential fp64 result; bf16 operands do not (5e-3 in emulation).
 //   * decay factors are products of a over row ranges inside a chunk, formed by
 //     multiplication: every factor is at most 1 except the column factor of the diagonal
-//     16x16 blocks of A_kk / A_qk, the inverse of the block's 16-token decay; a block decay
-//     below 2^-14 on any channel is flagged as KDA_DEVERR_DECAY_RANGE.
+//     16x16 blocks of A_kk / A_qk, the inverse of the block's 16-token decay. That factor is
+//     used only for key channels whose block decay is at least 2^-12 (so it stays <= 4096 in
+//     fp16); a channel that decays faster within a block is left out of that block's diagonal
+//     products and its terms k_r k_s prod_{s<t<=r} a_t are added in fp32 from the raw inputs,
+//     exact for any decay (reported as KDA_DEVERR_DECAY_RANGE, informational).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -51,7 +54,10 @@ constexpr int PNB = PC / 16;      // 16-row blocks per chunk
 constexpr int NPAIR = PNB * (PNB + 1) / 2;
 constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
 constexpr int PC16 = PC + 8;      // row pitch (halves) of [.][PC] fp16 arrays
-constexpr float DIAG_DECAY_MIN = 1.f / 16384.f;   // 2^-14
+// Smallest 16-token decay of a key channel whose diagonal-block terms go through the fp16
+// factorisation (column factor <= 2^12); below it the block's terms of that channel are
+// evaluated exactly in fp32.
+constexpr float DIAG_DECAY_MIN = 1.f / 4096.f;   // 2^-12
 constexpr int LDS_PER_CU = 160 * 1024;   // gfx950: LDS of one CU, the most one work-group may hold
 
 // ---- per-(chunk, head) operand block --------------------------------------------------------
@@ -210,6 +216,7 @@ struct PrepLds {
   float bp[PNB][PD];         // decay over each block: 2^(G_end(P) - G_start(P))
   _Float16 xvh[NPAIR][PD];   // 2^(G_start(P) - G_end(Q)) per pair, fp16
   float b[PC];
+  uint32_t xmask[PNB][PD / 32];   // channels whose block decay is below DIAG_DECAY_MIN
 };
 
 // pair index p = P(P+1)/2 + Q for Q <= P
@@ -329,6 +336,7 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
     *reinterpret_cast<f4*>(&L.u4.part[m4][c4]) = cpre[3];
   }
   if (t < PC) L.b[t] = t < n ? A.t.b[(size_t)(tok0 + t) * H + h] : 0.f;
+  if (t < PNB * PD / 32) (&L.xmask[0][0])[t] = 0u;
   __syncthreads();
 
   // ---- decayed fp16 operands: Ka/Qa (rows of block P times 2^(G - G_start(P))), F (times
@@ -350,9 +358,13 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
       const f4 bpv = p01 * p23;   // decay over the whole block
       *reinterpret_cast<f4*>(&L.bp[Pm][c4]) = bpv;
       if (Pm == PNB - 1) *reinterpret_cast<f4*>(blk + OFF_GAM + 4 * c4) = gsp * bpv;
-      if (bpv[0] < DIAG_DECAY_MIN || bpv[1] < DIAG_DECAY_MIN || bpv[2] < DIAG_DECAY_MIN ||
-          bpv[3] < DIAG_DECAY_MIN)
+      uint32_t fast = 0;   // the thread's four channels (one 32-channel word) that decay fast
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fast |= (bpv[e] < DIAG_DECAY_MIN ? 1u : 0u) << ((c4 + e) & 31);
+      if (fast) {
+        atomicOr(&L.xmask[Pm][c4 >> 5], fast);
         atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -407,9 +419,10 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
           // decay of the block when P = Q
         const int i0 = 2 * l;
         float z0, z1;
-        if (Pb == Q) {
-          z0 = __builtin_amdgcn_rcpf(L.bp[Q][i0]);
-          z1 = __builtin_amdgcn_rcpf(L.bp[Q][i0 + 1]);
+        if (Pb == Q) {   // 0 for the fast-decaying channels: their terms are added exactly below
+          const uint32_t fast = L.xmask[Q][i0 >> 5] >> (i0 & 31);
+          z0 = fast & 1u ? 0.f : __builtin_amdgcn_rcpf(L.bp[Q][i0]);
+          z1 = fast & 2u ? 0.f : __builtin_amdgcn_rcpf(L.bp[Q][i0 + 1]);
         } else {
           z0 = 1.f;
           z1 = 1.f;
@@ -429,6 +442,43 @@ __global__ __launch_bounds__(PNT, 2) void chunk_prep_kernel(PoolView P, PrefillL
         const half8 bb = ld8(&L.f16[16 * Q + l16][c]) * ld8(&L.xvh[p][c]);
         akk = mfma32(ld8(&L.ka[16 * Pb + l16][c]), bb, akk);
         aqk = mfma32(ld8(&L.qa[16 * Pb + l16][c]), bb, aqk);
+      }
+      if (Pb == Q) {
+        // Channels whose decay over this block is below DIAG_DECAY_MIN: their terms
+        // k_r k_s prod_{s<t<=r} a_t (A_kk, s < r) and q_r k_s prod_{s<t<=r} a_t (A_qk, s <= r)
+        // in fp32 from the raw inputs, for this lane's rows 4 lq + e and column s. Padded rows
+        // (past the chunk) read k = q = 0 and a = 1, as everywhere in this kernel.
+        const int s = l16, nb = n - 16 * Pb;   // rows of this block inside the chunk
+        const size_t blk0 = (size_t)(tok0 + 16 * Pb) * hstride + (size_t)h * PD;
+#pragma unroll 1
+        for (int wd = 0; wd < PD / 32; ++wd) {
+          uint32_t msk = (uint32_t)__builtin_amdgcn_readfirstlane((int)L.xmask[Q][wd]);
+          while (msk) {
+            const int i = 32 * wd + __builtin_ctz(msk);
+            msk &= msk - 1;
+            const float* ac = A.t.a + blk0 + i;
+            float run = 1.f, dec[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int tt = 0; tt < 16; ++tt, ac += hstride) {
+              const float a_t = tt < nb ? *ac : 1.f;
+              if (tt > s) run *= a_t;
+              if ((tt >> 2) == lq) dec[0] = (tt & 3) == 0 ? run : dec[0];
+              if ((tt >> 2) == lq) dec[1] = (tt & 3) == 1 ? run : dec[1];
+              if ((tt >> 2) == lq) dec[2] = (tt & 3) == 2 ? run : dec[2];
+              if ((tt >> 2) == lq) dec[3] = (tt & 3) == 3 ? run : dec[3];
+            }
+            const float ks = s < nb ? bf2f(A.t.k[blk0 + (size_t)s * hstride + i]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * lq + e;
+              const size_t off = blk0 + (size_t)r * hstride + i;
+              const float kr = r < nb ? bf2f(A.t.k[off]) : 0.f, qr = r < nb ? bf2f(A.t.q[off]) : 0.f;
+              const float w = ks * dec[e];
+              if (r > s) akk[e] = __builtin_fmaf(kr, w, akk[e]);
+              if (r >= s) aqk[e] = __builtin_fmaf(qr, w, aqk[e]);
+            }
+          }
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
