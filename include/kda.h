@@ -13,22 +13,23 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller. The library allocates and
- *     frees no device memory and synchronises only in kda_read_device_error, with two per-pool
- *     exceptions documented at kda_prefill_args and kda_mixed_batch: the fallback prefill
- *     workspace (when the caller passes none; grown after a device synchronise) and the side
- *     stream and events of kda_mixed_batch.
+ *     frees no device memory, creates no stream or event, and synchronises only in
+ *     kda_read_device_error: the prefill workspace and the side stream and events of a mixed
+ *     batch are the caller's too.
  *   - Token tensors are dense row-major: q, k [n][H][dk] bf16; v [n][H][dv] bf16;
  *     a [n][H][dk] fp32 (decay in (0,1)); b [n][H] fp32; o [n][H][dv] bf16.
  *     Device pointers must be 16-byte aligned.
  *   - Slot state is fp32 [num_slots][H][dk][dv] (row = key channel, column = value channel).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it only, apart
- *     from the part of a mixed batch forked to its side stream and joined back to `stream`.
+ *     from the part of a mixed batch forked to the caller's side stream and joined back to
+ *     `stream`.
  *   - Every call returns a kda_status; kda_last_error() gives a message for the last failure
  *     on the calling thread. A call rejected by its checks (any status but KDA_EHIP) enqueues
  *     no device work and changes no host state. KDA_EHIP means a HIP runtime call failed; part
  *     of the call's work may have been enqueued by then.
  *   - One pool is driven from one host thread at a time.
  *   - Supported shapes: dk == dv in {16, 128}; prefill chunk 16 (dk 16) or 64 (dk 128).
+ *     Both prefill shapes run the chunked form on the matrix cores.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -53,8 +54,10 @@ typedef enum {
 /* Device error bits, accumulated in the pool's device error word. */
 #define KDA_DEVERR_NACC_RANGE 1u   /* commit got n_accepted outside [0, verified-1]; clamped */
 #define KDA_DEVERR_SLOT_RANGE 2u   /* a device slot array held an id outside the pool; skipped */
-#define KDA_DEVERR_DECAY_RANGE 4u  /* prefill: a key channel decayed by more than 2^-14 within 16
-                                      tokens; the fp16 operand of that block may lose accuracy */
+#define KDA_DEVERR_DECAY_RANGE 4u  /* prefill, informational: a key channel decayed below 2^-12
+                                      within a 16-token block; that block's diagonal terms of the
+                                      channel were evaluated exactly in fp32 (slower path, same
+                                      accuracy) instead of through fp16 factors               */
 
 /* Pool geometry. ring_cap = positions a verify may hold (1 + max drafts), 1..64. */
 typedef struct {
@@ -91,7 +94,8 @@ size_t kda_meta_error_offset(const kda_pool_desc* desc);
  * EINVAL on null/misaligned pointers or bad sizes, EUNSUPPORTED on dk/dv not instantiated.  */
 kda_status kda_pool_create(const kda_pool_desc* desc, void* state, void* ring, void* meta,
                            kda_pool** out);
-/* Frees the host object only; the device buffers stay the caller's. */
+/* Frees the host object only (no device call, no synchronisation): the device buffers stay the
+ * caller's, and work already enqueued on them is the caller's to wait for.                    */
 kda_status kda_pool_destroy(kda_pool* pool);
 /* Allocates the lowest free slot index. ENOSLOT when none is free. Host only; the slot's
  * device state is whatever it last held -- call kda_slot_reset or write it by prefill.      */
@@ -125,11 +129,10 @@ kda_status kda_slot_checkpoint(kda_pool* pool, int32_t src, int32_t dst, void* s
  * copies drive validation, the device copies drive the kernels. Zero-length sequences are
  * allowed.
  * workspace: device memory, 256-byte aligned, of at least kda_prefill_workspace_bytes(pool,
- * n_tok, n_seq, chunk, ckpt_interval) bytes, owned by the caller and not touched by anything else until the
- * work on `stream` is done (the chunked form stages every chunk's S-independent operands there,
- * 65 KiB per chunk and head). NULL: the pool allocates its own buffer on first use and grows it
- * with hipMalloc (after a device synchronize) when a larger prefill comes; it is freed by
- * kda_pool_destroy. A workspace smaller than the need returns KDA_EWORKSPACE.            */
+ * n_tok, n_seq, chunk, ckpt_interval) bytes, owned by the caller and not touched by anything
+ * else until the work on `stream` is done (the chunked form at dk 128 stages every chunk's
+ * S-independent operands there, 60.5 KiB per chunk and head). A NULL or too small workspace
+ * where one is needed returns KDA_EWORKSPACE; the library never allocates one.            */
 typedef struct {
   const void* q; const void* k; const void* v;   /* bf16 */
   const float* a; const float* b;
@@ -144,7 +147,7 @@ typedef struct {
 /* Workspace bytes that any prefill of n_tok tokens in n_seq sequences with that checkpoint
  * interval needs (an upper bound over length mixes: at most floor(n_tok / chunk) + n_seq
  * chunks, plus floor(n_tok / ckpt_interval) when the interval is not a multiple of the
- * chunk); 0 where the token-by-token kernel runs (dk = 16) or for n_seq <= 0.              */
+ * chunk); 0 where none is needed (dk = 16 keeps every chunk on chip) or for n_seq <= 0.    */
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
                                    int32_t chunk, int32_t ckpt_interval);
 kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);
@@ -227,11 +230,14 @@ kda_status kda_commit_direct(kda_pool* pool, int32_t B, const int32_t* h_slots,
  * o is written in the same packing, with no gather or scatter; the prefill's token pointers
  * and the step slot arrays of `prefill`, `decode` and `verify` are ignored in favour of the
  * packed ones below. Commit, decode and verify touch only their own slots, so when the batch
- * also has a prefill they run (in that order) on a side stream owned by the pool (default priority, created on
- * first use, destroyed by kda_pool_destroy) while the prefill's kernels run on `stream`:
- * forked by an event recorded on `stream` before the prefill's first kernel, joined by an
- * event that `stream` waits on before the call returns. Everything enqueued on `stream`
- * afterwards is ordered after all three parts.                                           */
+ * also has a prefill and the caller gives a side stream they run (in that order) on that side
+ * stream while the prefill's kernels run on `stream`: forked by fork_event, recorded on
+ * `stream` before the prefill's first kernel, joined by join_event, recorded on the side
+ * stream and waited on by `stream` before the call returns. Everything enqueued on `stream`
+ * afterwards is ordered after all three parts. side_stream NULL: the three parts run in order
+ * on `stream` ahead of the prefill. The side stream (default priority) and both events
+ * (timing may be disabled) are the caller's; a call that uses them must not overlap another
+ * call using the same events.                                                            */
 typedef struct {
   const void* q; const void* k; const void* v;   /* bf16 [n_total][H][d] */
   const float* a; const float* b;
@@ -247,6 +253,9 @@ typedef struct {
   int32_t n_commit;
   const int32_t* h_commit_slots; const int32_t* d_commit_slots;
   const int32_t* d_n_accepted;
+  void* side_stream;   /* hipStream_t or NULL                                             */
+  void* fork_event;    /* hipEvent_t, required with a side stream                         */
+  void* join_event;    /* hipEvent_t, required with a side stream                         */
 } kda_mixed_args;
 kda_status kda_mixed_batch(kda_pool* pool, const kda_mixed_args* args, void* stream);
 

@@ -58,7 +58,8 @@ class kda_mixed_args(ctypes.Structure):
                 ("d_decode_slots", c_void_p), ("n_verify", c_int32), ("n_pos", c_int32),
                 ("h_verify_slots", c_void_p), ("d_verify_slots", c_void_p),
                 ("n_commit", c_int32), ("h_commit_slots", c_void_p), ("d_commit_slots", c_void_p),
-                ("d_n_accepted", c_void_p)]
+                ("d_n_accepted", c_void_p), ("side_stream", c_void_p), ("fork_event", c_void_p),
+                ("join_event", c_void_p)]
 
 
 # name -> (restype, argtypes); every symbol include/kda.h declares.

@@ -1,6 +1,7 @@
 // Host side of the KDA engine: pool geometry, slot free list and idle/pending state
-// machine, argument validation, and dispatch to the kernel launchers. No device memory is
-// allocated here; every device buffer belongs to the caller.
+// machine, argument validation, and dispatch to the kernel launchers. The library allocates no
+// device memory and creates no stream or event: every device buffer, the prefill workspace, and
+// the side stream and events of a mixed batch belong to the caller.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -68,12 +69,6 @@ struct kda_pool {
   std::vector<int32_t> draft_npos, draft_index;
   std::vector<uint32_t> stamp;         // distinctness checks
   uint32_t epoch = 0;
-  void* ws = nullptr;                  // prefill workspace used when the caller passes none
-  size_t ws_bytes = 0;
-  // Side stream of mixed batches (default priority): decode and verify run there while the
-  // prefill's sequential pass runs on the caller's stream. Created on first use.
-  hipStream_t aux = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
   // Mark-and-check: returns false if a slot repeats within one validation pass.
   void begin_pass() {
@@ -207,11 +202,6 @@ kda_status kda_pool_create(const kda_pool_desc* d, void* state, void* ring, void
 
 kda_status kda_pool_destroy(kda_pool* p) {
   if (!p) return fail(KDA_EINVAL, "null pool");
-  if (p->ws || p->aux) (void)hipDeviceSynchronize();
-  if (p->ws) (void)hipFree(p->ws);
-  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
-  if (p->ev_join) (void)hipEventDestroy(p->ev_join);
-  if (p->aux) (void)hipStreamDestroy(p->aux);
   delete p;
   return KDA_OK;
 }
@@ -341,38 +331,21 @@ static kda_status validate_prefill(kda_pool* p, const kda_prefill_args* a, bool 
   return KDA_OK;
 }
 
-// Device workspace of a prefill: the caller's buffer, checked against the need, or (when the
-// caller passes none) the pool's own buffer, grown on demand.
+// Device workspace of a prefill: the caller's buffer, checked against the need. The library
+// never allocates one itself.
 static kda_status prefill_workspace(kda_pool* p, const kda_prefill_args* a, int64_t n_chunks,
                                     void** ws) {
   const size_t need =
       kda::prefill_workspace_bytes(p->desc.dk, a->chunk, p->desc.num_heads, a->n_seq, n_chunks);
   *ws = nullptr;
   if (need == 0) return KDA_OK;
-  if (a->workspace) {
-    if (a->workspace_bytes < need)
-      return fail(KDA_EWORKSPACE, "workspace of %zu bytes, this prefill needs %zu",
-                  a->workspace_bytes, need);
-    if (!aligned(a->workspace, 256)) return fail(KDA_EINVAL, "workspace must be 256-byte aligned");
-    *ws = a->workspace;
-    return KDA_OK;
-  }
-  if (p->ws_bytes < need) {
-    if (p->ws) {
-      hipError_t e = hipDeviceSynchronize();   // earlier prefills may still read the old buffer
-      if (e != hipSuccess) return hip_fail(e, "workspace grow");
-      (void)hipFree(p->ws);
-      p->ws = nullptr;
-      p->ws_bytes = 0;
-    }
-    hipError_t e = hipMalloc(&p->ws, need);
-    if (e != hipSuccess) {
-      p->ws = nullptr;
-      return hip_fail(e, "workspace allocation");
-    }
-    p->ws_bytes = need;
-  }
-  *ws = p->ws;
+  if (!a->workspace)
+    return fail(KDA_EWORKSPACE, "no workspace given, this prefill needs %zu bytes", need);
+  if (a->workspace_bytes < need)
+    return fail(KDA_EWORKSPACE, "workspace of %zu bytes, this prefill needs %zu",
+                a->workspace_bytes, need);
+  if (!aligned(a->workspace, 256)) return fail(KDA_EINVAL, "workspace must be 256-byte aligned");
+  *ws = a->workspace;
   return KDA_OK;
 }
 
@@ -453,6 +426,8 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   if (!p || !m) return fail(KDA_EINVAL, "null argument");
   const int32_t H = p->desc.num_heads, dk = p->desc.dk, dv = p->desc.dv;
   if (m->n_decode < 0 || m->n_verify < 0 || m->n_commit < 0) return fail(KDA_EINVAL, "negative batch");
+  if (m->side_stream && (!m->fork_event || !m->join_event))
+    return fail(KDA_EINVAL, "a side stream needs its fork and join events");
   if (m->n_verify > 0 && (m->n_pos < 1 || m->n_pos > p->desc.ring_cap))
     return fail(KDA_EINVAL, "n_pos %d outside 1..ring_cap", m->n_pos);
   kda_status st = check_tensors(m->q, m->k, m->v, m->a, m->b, m->o);
@@ -510,15 +485,16 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
   };
   // Commit, decode and verify touch only their own slots (checked distinct from the
   // prefill's above), so they need no order against the prefill: with a prefill in the batch
-  // they go to the side stream, in that order, ahead of the prefill's kernels, and the caller's
-  // stream waits for them before anything later. They then run beside the prefill's
-  // S-independent kernel (whose work-groups leave room on each CU) and are done before its
-  // sequential pass starts, which therefore keeps every CU and its width plan.
+  // and a side stream given they go to the side stream, in that order, ahead of the prefill's
+  // kernels, and the caller's stream waits for them before anything later. They then run beside
+  // the prefill's S-independent kernel (whose work-groups leave room on each CU) and are done
+  // before its sequential pass starts, which therefore keeps every CU and its width plan.
   struct StepLaunches {
     kda_pool* p;
     const kda_mixed_args* m;
     kda::StepTensors dec, ver;
-    hipStream_t s;
+    hipStream_t s, aux;
+    hipEvent_t ev_fork, ev_join;
     bool fork;
     hipError_t run(hipStream_t on) const {
       hipError_t e = hipSuccess;
@@ -535,22 +511,18 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
       return e;
     }
     hipError_t forked() const {
-      hipError_t e = hipEventRecord(p->ev_fork, s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_fork, 0);
-      if (e == hipSuccess) e = run(p->aux);
-      if (e == hipSuccess) e = hipEventRecord(p->ev_join, p->aux);
+      hipError_t e = hipEventRecord(ev_fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(aux, ev_fork, 0);
+      if (e == hipSuccess) e = run(aux);
+      if (e == hipSuccess) e = hipEventRecord(ev_join, aux);
       return e;
     }
   };
   const bool steps = m->n_decode > 0 || m->n_verify > 0 || m->n_commit > 0;
-  StepLaunches sl{p, m, part(n_pre), part(n_pre + m->n_decode), s, pre.n_seq > 0 && steps};
+  StepLaunches sl{p, m, part(n_pre), part(n_pre + m->n_decode), s, as_stream(m->side_stream),
+                  static_cast<hipEvent_t>(m->fork_event), static_cast<hipEvent_t>(m->join_event),
+                  pre.n_seq > 0 && steps && m->side_stream != nullptr};
   hipError_t e = hipSuccess;
-  if (sl.fork && !p->aux) {
-    e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming);
-    if (e != hipSuccess) return keep_pending(hip_fail(e, "mixed: side stream"));
-  }
   if (pre.n_seq > 0) {
     void* ws = nullptr;
     st = prefill_workspace(p, &pre, n_chunks, &ws);
@@ -562,11 +534,14 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     if (sl.fork) {
       e = sl.forked();
       if (e != hipSuccess) return hip_fail(e, "mixed: side stream");
+    } else if (steps) {
+      e = sl.run(s);
+      if (e != hipSuccess) return hip_fail(e, "mixed: commit / decode / verify launch");
     }
     e = kda::launch_prefill(p->view, L, s);
     if (e != hipSuccess) return hip_fail(e, "mixed: prefill launch");
     if (sl.fork) {
-      e = hipStreamWaitEvent(s, p->ev_join, 0);
+      e = hipStreamWaitEvent(s, sl.ev_join, 0);
       if (e != hipSuccess) return hip_fail(e, "mixed: join");
     }
   } else if (steps) {

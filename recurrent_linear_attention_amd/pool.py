@@ -1,9 +1,10 @@
 """Python binding of the KDA C ABI: the same entry points, taking torch tensors.
 
-Argument marshalling only -- torch provides device memory and the current HIP stream, the
-library (``lib/libkda.so``) does all the work. Index arrays given as plain sequences are
-copied to the device on torch's current stream, so calls should run on that stream. ``KDAPool`` owns the three caller-side device
-buffers (state, ReplaySSM ring, metadata) and the library's pool handle.
+Argument marshalling only -- torch provides device memory, streams and events, the library
+(``lib/libkda.so``) does all the work. Index arrays given as plain sequences are copied to the
+device on torch's current stream, so calls should run on that stream. ``KDAPool`` owns the
+caller-side device buffers (state, ReplaySSM ring, metadata, the prefill workspace), the side
+stream and events of mixed batches, and the library's pool handle.
 """
 from __future__ import annotations
 
@@ -110,7 +111,8 @@ class KDAPool:
         check(lib.kda_ring_layout(byref(self.desc), off), "kda_ring_layout")
         self.ring_offsets = list(off)
         self.err_offset = lib.kda_meta_error_offset(byref(self.desc))
-        self._ws = None   # prefill workspace (torch allocation, grown on demand)
+        self._ws = None     # prefill workspace (torch allocation, grown on demand)
+        self._side = None   # side stream + fork / join events of mixed batches (created on first use)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -259,10 +261,11 @@ class KDAPool:
     def kda_mixed_batch(self, q, k, v, a, b, cu_seqlens, out_slots, decode_slots,
                         verify_slots, n_pos: int, init_slots=None, ckpt_slots=None,
                         ckpt_interval: int = 0, o=None, stream=None, commit_slots=None,
-                        n_accepted: torch.Tensor | None = None) -> torch.Tensor:
+                        n_accepted: torch.Tensor | None = None, fork: bool = True) -> torch.Tensor:
         """One packed batch [prefill tokens | decode tokens | verify tokens ([seq][pos])].
         commit_slots / n_accepted (device int32): ReplaySSM commits of slots pending from an
-        earlier verify, run before this batch's decode and verify."""
+        earlier verify, run before this batch's decode and verify. fork: run those parts on the
+        pool's side stream beside the prefill (False: in order on `stream`, ahead of it)."""
         if o is None:
             o = torch.empty(q.shape[:-1] + (self.d,), dtype=torch.bfloat16, device=q.device)
         ptrs = self._tok_ptrs(q, k, v, a, b, o)
@@ -282,8 +285,25 @@ class KDAPool:
             com = _ix(commit_slots, self.device)
             m.n_commit, m.h_commit_slots, m.d_commit_slots = com.np.size, com.h, com.d
             m.d_n_accepted = _dev(n_accepted, torch.int32, "n_accepted")
+        if fork and m.prefill.n_seq > 0 and (m.n_decode or m.n_verify or m.n_commit):
+            side, ev_fork, ev_join = self._side_stream()
+            m.side_stream, m.fork_event, m.join_event = side.cuda_stream, ev_fork, ev_join
         check(lib.kda_mixed_batch(self.handle, byref(m), _stream(stream)), "kda_mixed_batch")
         return o
+
+    def _side_stream(self):
+        """Side stream (default priority) and fork / join events for mixed batches, from torch.
+        torch creates an event's HIP handle when it is first recorded, so both are recorded once
+        here before their handles are passed on."""
+        if self._side is None:
+            side = torch.cuda.Stream(device=self.device)
+            evs = [torch.cuda.Event(), torch.cuda.Event()]
+            for e in evs:
+                e.record(side)
+            side.synchronize()
+            self._side = (side, evs)
+        side, evs = self._side
+        return side, evs[0].cuda_event, evs[1].cuda_event
 
     def kda_prefill_plan(self, cu_seqlens) -> list:
         """Width plan of kda_prefill's state pass for these sequence boundaries:

@@ -234,6 +234,24 @@ def test_prefill_workspace_size_and_checks():
     assert b"workspace" in lib.kda_last_error()
     a.workspace, a.workspace_bytes = FAKE + 16, need
     assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EINVAL
+    # no workspace at all: rejected, never allocated by the library
+    a.workspace, a.workspace_bytes = None, 0
+    assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EWORKSPACE
+    assert b"no workspace" in lib.kda_last_error()
+    a.workspace_bytes = need
+    assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EWORKSPACE
+
+
+def test_mixed_batch_side_stream_needs_both_events():
+    p = HostPool()
+    s = [p.alloc()[1] for _ in range(3)]
+    m, _keep = mixed_args(i32(0, 32), i32(s[0]), dec=[s[1]])
+    m.side_stream, m.fork_event, m.join_event = FAKE, FAKE, None
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    assert b"fork and join events" in lib.kda_last_error()
+    m.fork_event, m.join_event = None, FAKE
+    assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
+    assert lib.kda_slot_host_state(p.h, s[1]) == 1
 
 
 def test_mixed_batch_rejects_slot_overlap():
