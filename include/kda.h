@@ -151,6 +151,18 @@ typedef struct {
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int32_t n_tok, int32_t n_seq,
                                    int32_t chunk, int32_t ckpt_interval);
 kda_status kda_prefill(kda_pool* pool, const kda_prefill_args* args, void* stream);
+/* ---- prefill without allocation: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation) ---------------
+ * kda_prefill with its workspace taken from a scratch area inside the library
+ * (KDA_PREFILL_SCRATCH_BYTES per GPU, held from the library's first use on that GPU until the
+ * process ends); args->workspace and workspace_bytes are ignored, and the call allocates
+ * nothing. A prefill whose workspace need (kda_prefill_workspace_bytes for its lengths)
+ * exceeds KDA_PREFILL_SCRATCH_BYTES returns KDA_EWORKSPACE before any device work. Every call
+ * on a GPU shares that GPU's scratch, which keeps the last call's contents (a call needs none
+ * of them): calls that overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller. Results are bit-identical to kda_prefill's.                      */
+#define KDA_PREFILL_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_prefill_noalloc(kda_pool* pool, const kda_prefill_args* args, void* stream);
 /* Width plan of kda_prefill's sequential (inter-chunk) pass for sequences with host lengths
  * h_cu_seqlens[0..n_seq] on the current device (the chunked form, dk = 128): returns the number
  * of groups G (1..4) and fills rank_end[0..G-1] and vsw[0..G-1] (caller arrays of 4): the

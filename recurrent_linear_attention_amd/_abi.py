@@ -78,6 +78,7 @@ PROTOTYPES = {
     "kda_slot_checkpoint": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
     "kda_prefill_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32, c_int32, c_int32]),
     "kda_prefill": (c_int32, [c_void_p, POINTER(kda_prefill_args), c_void_p]),
+    "kda_prefill_noalloc": (c_int32, [c_void_p, POINTER(kda_prefill_args), c_void_p]),
     "kda_prefill_plan": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "kda_decode": (c_int32, [c_void_p, POINTER(kda_step_args), c_void_p]),
     "kda_verify": (c_int32, [c_void_p, POINTER(kda_step_args), c_int32, c_void_p]),

@@ -78,6 +78,11 @@ StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H);
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);
 // Token-by-token prefill with the decode step (reference-form kernel; any supported d).
 hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
+// Scratch of the allocation-free prefill: a file-scope device array of this many bytes in the
+// prefill's code object; prefill_scratch returns its address on the current device (looked up
+// once per device).
+constexpr size_t PREFILL_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t prefill_scratch(void** out);
 
 // Chunking of one sequence of len tokens with checkpoints every `interval` tokens (0: none).
 // Every checkpoint position ends a chunk ("vLLM lifts Kimi K3 throughput by up to 2.8x",

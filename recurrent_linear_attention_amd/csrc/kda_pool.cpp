@@ -349,6 +349,16 @@ static kda_status prefill_workspace(kda_pool* p, const kda_prefill_args* a, int6
   return KDA_OK;
 }
 
+static kda_status run_prefill(kda_pool* p, const kda_prefill_args* a, int32_t max_len,
+                              int64_t n_chunks, void* ws, void* stream) {
+  kda::PrefillLaunch L{tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->n_seq, a->n_tok,
+                       a->chunk, a->ckpt_interval, a->d_cu_seqlens, a->d_init_slot,
+                       a->d_out_slot, a->d_ckpt_slot, max_len, n_chunks, ws};
+  L.plan = kda::plan_state_pass(a->h_cu_seqlens, a->n_seq, p->desc.num_heads);
+  hipError_t e = kda::launch_prefill(p->view, L, as_stream(stream));
+  return e == hipSuccess ? KDA_OK : hip_fail(e, "prefill launch");
+}
+
 kda_status kda_prefill(kda_pool* p, const kda_prefill_args* a, void* stream) {
   int32_t max_len = 0;
   int64_t n_chunks = 0;
@@ -358,12 +368,30 @@ kda_status kda_prefill(kda_pool* p, const kda_prefill_args* a, void* stream) {
   void* ws = nullptr;
   st = prefill_workspace(p, a, n_chunks, &ws);
   if (st != KDA_OK) return st;
-  kda::PrefillLaunch L{tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->n_seq, a->n_tok,
-                       a->chunk, a->ckpt_interval, a->d_cu_seqlens, a->d_init_slot,
-                       a->d_out_slot, a->d_ckpt_slot, max_len, n_chunks, ws};
-  L.plan = kda::plan_state_pass(a->h_cu_seqlens, a->n_seq, p->desc.num_heads);
-  hipError_t e = kda::launch_prefill(p->view, L, as_stream(stream));
-  return e == hipSuccess ? KDA_OK : hip_fail(e, "prefill launch");
+  return run_prefill(p, a, max_len, n_chunks, ws, stream);
+}
+
+static_assert(KDA_PREFILL_SCRATCH_BYTES == kda::PREFILL_SCRATCH_BYTES, "scratch size in the header");
+
+kda_status kda_prefill_noalloc(kda_pool* p, const kda_prefill_args* a, void* stream) {
+  int32_t max_len = 0;
+  int64_t n_chunks = 0;
+  kda_status st = validate_prefill(p, a, true, &max_len, &n_chunks);
+  if (st != KDA_OK) return st;
+  if (a->n_seq == 0) return KDA_OK;
+  const size_t need =
+      kda::prefill_workspace_bytes(p->desc.dk, a->chunk, p->desc.num_heads, a->n_seq, n_chunks);
+  if (need > kda::PREFILL_SCRATCH_BYTES)
+    return fail(KDA_EWORKSPACE,
+                "this prefill needs %zu bytes of workspace; kda_prefill_noalloc holds %zu "
+                "(split the prefill, or call kda_prefill with a workspace)",
+                need, (size_t)kda::PREFILL_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = kda::prefill_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+  }
+  return run_prefill(p, a, max_len, n_chunks, ws, stream);
 }
 
 kda_status kda_decode(kda_pool* p, const kda_step_args* a, void* stream) {

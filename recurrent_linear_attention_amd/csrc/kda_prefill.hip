@@ -37,8 +37,15 @@
 //     exact for any decay (reported as KDA_DEVERR_DECAY_RANGE, informational).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
+
+// Workspace of kda_prefill_noalloc, for callers that cannot allocate device memory: every GPU
+// the library runs on holds one copy until the process ends. Host code never uses this name as
+// an address (it is a host-side stand-in there): prefill_scratch looks the device address up.
+static __device__ __align__(256) char scratch[kda::PREFILL_SCRATCH_BYTES];
 
 namespace kda {
 namespace {
@@ -1029,6 +1036,28 @@ hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t
 }
 
 }  // namespace
+
+hipError_t prefill_scratch(void** out) {
+  // Device address of `scratch` on the current device, looked up once per device (each GPU
+  // holds its own copy at its own address) and kept for later calls.
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* per_device[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    per_device[dev] = ptr;
+  }
+  *out = per_device[dev];
+  return hipSuccess;
+}
 
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks) {
   if (dk != PD || chunk != PC || n_seq <= 0) return 0;

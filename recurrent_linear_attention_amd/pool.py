@@ -77,6 +77,9 @@ class IndexArray:
         self.np = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
         self.dev = torch.from_numpy(self.np).to(device, non_blocking=False)
 
+    def __len__(self):
+        return int(self.np.size)
+
     @property
     def h(self):
         return self.np.ctypes.data if self.np.size else None
@@ -186,6 +189,28 @@ class KDAPool:
                                     chunk or chunk_for(self.d), ckpt_interval,
                                     self._tok_ptrs(q, k, v, a, b, o))
         check(lib.kda_prefill(self.handle, byref(args), _stream(stream)), "kda_prefill")
+        return o
+
+    def kda_prefill_noalloc(self, q, k, v, a, b, cu_seqlens, out_slots, o, init_slots=None,
+                            ckpt_slots=None, ckpt_interval: int = 0, stream=None) -> torch.Tensor:
+        """kda_prefill with the library's scratch as workspace (kda_prefill_noalloc): nothing is
+        allocated for the call. o and, to keep the call free of allocations, IndexArray
+        arguments are the caller's."""
+        n_tok = q.shape[0]
+        cu = _ix(cu_seqlens, self.device)
+        out = _ix(out_slots, self.device)
+        init = None if init_slots is None else _ix(init_slots, self.device)
+        ckpt = None if ckpt_slots is None or len(ckpt_slots) == 0 else _ix(ckpt_slots, self.device)
+        args = _abi.kda_prefill_args(*self._tok_ptrs(q, k, v, a, b, o))
+        args.n_seq, args.n_tok = cu.np.size - 1, n_tok
+        args.chunk, args.ckpt_interval = chunk_for(self.d), ckpt_interval
+        args.h_cu_seqlens, args.d_cu_seqlens = cu.h, cu.d
+        if init is not None:
+            args.h_init_slot, args.d_init_slot = init.h, init.d
+        args.h_out_slot, args.d_out_slot = out.h, out.d
+        if ckpt is not None:
+            args.h_ckpt_slot, args.d_ckpt_slot = ckpt.h, ckpt.d
+        check(lib.kda_prefill_noalloc(self.handle, byref(args), _stream(stream)), "kda_prefill_noalloc")
         return o
 
     def _step_args(self, q, k, v, a, b, o, slots):

@@ -242,6 +242,22 @@ def test_prefill_workspace_size_and_checks():
     assert lib.kda_prefill(p.h, byref(a), None) == _abi.KDA_EWORKSPACE
 
 
+def test_prefill_noalloc_rejects_prefills_beyond_its_scratch():
+    # one 4096-token prompt at 32 heads needs 65 chunks x 32 x 61,952 bytes > 64 MiB: rejected
+    # before any device call, nothing allocated, slots unchanged
+    p = HostPool(n=4, H=32, d=128)
+    s = [p.alloc()[1] for _ in range(2)]
+    a = prefill_args(i32(0, 4096), i32(s[0]), chunk=64)
+    assert lib.kda_prefill_workspace_bytes(p.h, 4096, 1, 64, 0) > 64 << 20
+    assert lib.kda_prefill_noalloc(p.h, byref(a), None) == _abi.KDA_EWORKSPACE
+    assert b"kda_prefill_noalloc holds 67108864" in lib.kda_last_error()
+    # argument checks come first, as in kda_prefill
+    assert lib.kda_prefill_noalloc(p.h, byref(prefill_args(i32(0, 40), i32(s[0]), chunk=32)), None) \
+        == _abi.KDA_EUNSUPPORTED
+    assert lib.kda_prefill_noalloc(p.h, byref(prefill_args(i32(0), i32(), chunk=64)), None) == 0
+    assert [lib.kda_slot_host_state(p.h, x) for x in s] == [1, 1]
+
+
 def test_mixed_batch_side_stream_needs_both_events():
     p = HostPool()
     s = [p.alloc()[1] for _ in range(3)]
