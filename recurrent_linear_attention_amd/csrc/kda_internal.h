@@ -74,10 +74,8 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
 // latency / CU-time model of the pass; beyond 64 sequences one width for all.
 StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H);
 // Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
-// shapes that run the token-by-token kernel).
+// d = 16, whose chunked form keeps every chunk on chip).
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);
-// Token-by-token prefill with the decode step (reference-form kernel; any supported d).
-hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s);
 // Scratch of the allocation-free prefill: a file-scope device array of this many bytes in the
 // prefill's code object; prefill_scratch returns its address on the current device (looked up
 // once per device).

@@ -1005,6 +1005,218 @@ __global__ __launch_bounds__(64 * (SCW + SLW)) void state_pass_kernel(PoolView P
   }
 }
 
+// ---- d = 16: the chunked form of one (sequence, head) in one wave -------------------------------
+// With d = 16 and chunk 16 a chunk's operands are single 16 x 16 tiles, so a wave keeps the whole
+// chunked form on chip -- no operand blocks, no workspace -- and runs every product on
+// v_mfma_f32_16x16x4_f32 (fp32 operands and accumulation). Lane L = i16 + 16 g:
+//   * as an A / B operand at step s of a K = 16 product it holds element (i16, 4 g + s): row i16
+//     of A, column i16 of B, index 4 g + s of the contracted dimension;
+//   * as an accumulator it holds rows 4 g .. 4 g + 3 of column i16 -- which is exactly the B
+//     operand of the next product, so the state S (rows = key channels), X and W pass from one
+//     product to the next in registers.
+// Per chunk (decays from the chunk start, D_r = prod_{t<=r} a_t, E_s = prod_{t>s} a_t):
+//   A_kk = (K D)(K / D)^T (s < r), A_qk = (Q D)(K / D)^T (s <= r), T = (I + Diag(b) A_kk)^-1 Diag(b),
+//   X = V - (K D) S, W = T X, O = (Q D) S + A_qk W, S' = Diag(D_15) S + (K E)^T W.
+// A key channel whose decay over the chunk is below 2^-60 (where 1 / D could leave the fp32
+// range) takes no part in the factored A products; its terms k_r k_s prod_{s<t<=r} a_t are added
+// exactly from the raw inputs instead (KDA_DEVERR_DECAY_RANGE, informational).
+constexpr int SD = 16;                          // head dim of this form
+constexpr int SC = 16;                          // its chunk
+constexpr float SMALL_CHUNK_DECAY_MIN = 0x1p-60f;
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// value of lane l - N (row_shr) or l + N (row_shl) inside the lane's 16-lane row, 1 past its ends
+template <int CTRL>
+__device__ __forceinline__ float row_shift_or_one(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+struct SmallLds {
+  float m[3][SC][SC + 1];   // Diag(b) A_kk, then T; A_qk; K E (token-major)
+  float b[SC];
+};
+
+__global__ __launch_bounds__(64) void prefill_small_kernel(PoolView P, PrefillLaunch A) {
+  __shared__ SmallLds L;
+  const int H = P.H, h = blockIdx.x % H, si = blockIdx.x / H;
+  const int l = threadIdx.x, i16 = l & 15, g = l >> 4;
+  const int lo = A.cu_seqlens[si], len = A.cu_seqlens[si + 1] - lo;
+  const int nch = seq_chunks(len, SC, A.ckpt_interval);
+  int ck = 0;   // first checkpoint entry of this sequence
+  if (A.ckpt_interval > 0)
+    for (int j = 0; j < si; ++j) ck += (A.cu_seqlens[j + 1] - A.cu_seqlens[j]) / A.ckpt_interval;
+  const int init = A.init_slot ? A.init_slot[si] : -1;
+  const bool has_init = init >= 0 && init < P.num_slots;
+  const size_t per = (size_t)H * SD * SD, hoff = (size_t)h * SD * SD, hs = (size_t)H * SD;
+  const int64_t pos0 = has_init ? P.meta[init].pos : 0;
+  f4 S;   // S[4 g + e][i16]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) S[e] = has_init ? P.state[init * per + hoff + (4 * g + e) * SD + i16] : 0.f;
+
+  for (int c = 0; c < nch; ++c) {
+    int t0, n;
+    chunk_span(c, len, SC, A.ckpt_interval, &t0, &n);
+    const size_t base = (size_t)(lo + t0) * hs + (size_t)h * SD;   // token 0 of the chunk, this head
+    // row i16, channels 4 g .. 4 g + 3; padded rows: k = q = v = 0, a = 1, b = 0
+    const bool live = i16 < n;
+    f4 av = {1.f, 1.f, 1.f, 1.f}, kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
+    if (live) {
+      const float4 a4 = *reinterpret_cast<const float4*>(A.t.a + base + (size_t)i16 * hs + 4 * g);
+      av = f4{a4.x, a4.y, a4.z, a4.w};
+      const uint2 kw = *reinterpret_cast<const uint2*>(A.t.k + base + (size_t)i16 * hs + 4 * g);
+      const uint2 qw = *reinterpret_cast<const uint2*>(A.t.q + base + (size_t)i16 * hs + 4 * g);
+      kv = f4{bf2f(kw.x & 0xffffu), bf2f(kw.x >> 16), bf2f(kw.y & 0xffffu), bf2f(kw.y >> 16)};
+      qv = f4{bf2f(qw.x & 0xffffu), bf2f(qw.x >> 16), bf2f(qw.y & 0xffffu), bf2f(qw.y >> 16)};
+    }
+    f4 X;   // starts as V[4 g + e][i16]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[e] = 4 * g + e < n ? bf2f(A.t.v[base + (size_t)(4 * g + e) * hs + i16]) : 0.f;
+    if (g == 0) L.b[i16] = live ? A.t.b[(size_t)(lo + t0 + i16) * H + h] : 0.f;
+
+    // decays down the rows (the lanes of each 16-lane row): inclusive prefix D, exclusive suffix E
+    f4 Dp, Es;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      float d = av[sidx];
+      d *= row_shift_or_one<0x111>(d);
+      d *= row_shift_or_one<0x112>(d);
+      d *= row_shift_or_one<0x114>(d);
+      d *= row_shift_or_one<0x118>(d);
+      Dp[sidx] = d;
+      float e = row_shift_or_one<0x101>(av[sidx]);
+      e *= row_shift_or_one<0x101>(e);
+      e *= row_shift_or_one<0x102>(e);
+      e *= row_shift_or_one<0x104>(e);
+      e *= row_shift_or_one<0x108>(e);
+      Es[sidx] = e;
+    }
+    // the chunk's decay of channel 4 g + s (row 15 of this lane group)
+    f4 gam;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) gam[sidx] = __shfl(Dp[sidx], 16 * g + 15);
+    uint32_t fast = 0;   // channels (bit = channel) below SMALL_CHUNK_DECAY_MIN
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      const uint64_t bal = __ballot(i16 == 0 && gam[sidx] < SMALL_CHUNK_DECAY_MIN);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) fast |= (uint32_t)((bal >> (16 * gg)) & 1u) << (4 * gg + sidx);
+    }
+    fast = (uint32_t)__builtin_amdgcn_readfirstlane((int)fast);
+    if (fast && l == 0) atomicOr(P.err, (uint32_t)KDA_DEVERR_DECAY_RANGE);
+
+    f4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      const float ki = (fast >> (4 * g + sidx)) & 1u ? 0.f : kv[sidx] / Dp[sidx];
+      akk = mfma4(kv[sidx] * Dp[sidx], ki, akk);
+      aqk = mfma4(qv[sidx] * Dp[sidx], ki, aqk);
+    }
+    if (fast) {   // exact terms of the fast channels: column i16, rows 4 g + e
+      const size_t cb = (size_t)(lo + t0) * hs + (size_t)h * SD;
+      uint32_t msk = fast;
+      while (msk) {
+        const int ch = __builtin_ctz(msk);
+        msk &= msk - 1;
+        float run = 1.f, dec[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int tt = 0; tt < SC; ++tt) {
+          const float a_t = tt < n ? A.t.a[cb + (size_t)tt * hs + ch] : 1.f;
+          if (tt > i16) run *= a_t;
+          if ((tt >> 2) == g) dec[0] = (tt & 3) == 0 ? run : dec[0];
+          if ((tt >> 2) == g) dec[1] = (tt & 3) == 1 ? run : dec[1];
+          if ((tt >> 2) == g) dec[2] = (tt & 3) == 2 ? run : dec[2];
+          if ((tt >> 2) == g) dec[3] = (tt & 3) == 3 ? run : dec[3];
+        }
+        const float ks = i16 < n ? bf2f(A.t.k[cb + (size_t)i16 * hs + ch]) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float kr = r < n ? bf2f(A.t.k[cb + (size_t)r * hs + ch]) : 0.f;
+          const float qr = r < n ? bf2f(A.t.q[cb + (size_t)r * hs + ch]) : 0.f;
+          const float wgt = ks * dec[e];
+          if (r > i16) akk[e] = __builtin_fmaf(kr, wgt, akk[e]);
+          if (r >= i16) aqk[e] = __builtin_fmaf(qr, wgt, aqk[e]);
+        }
+      }
+    }
+    __syncthreads();   // b landed; the previous chunk's readers of m[] are done
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      L.m[0][r][i16] = i16 < r ? L.b[r] * akk[e] : 0.f;   // Diag(b) A_kk, strictly lower
+      L.m[1][r][i16] = i16 <= r ? aqk[e] : 0.f;           // A_qk, lower
+    }
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) L.m[2][i16][4 * g + sidx] = kv[sidx] * Es[sidx];   // K E
+    __syncthreads();
+    // T = (I + Diag(b) A_kk)^-1 Diag(b): lanes 0..15 each solve one column j by forward
+    // substitution, then scale it by b_j; written over Diag(b) A_kk row by row (row r is read
+    // only by rows after it, and each lane works on its own column)
+    if (l < SC) {
+      const int j = l;
+      float x[SC];
+#pragma unroll
+      for (int r = 0; r < SC; ++r) {
+        float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) acc = __builtin_fmaf(-L.m[0][r][m], x[m], acc);
+        x[r] = acc;
+      }
+      const float bj = L.b[j];
+#pragma unroll
+      for (int r = 0; r < SC; ++r) L.m[0][r][j] = x[r] * bj;
+    }
+    __syncthreads();
+
+    // X = V - (K D) S; W = T X; O = (Q D) S + A_qk W; S' = Diag(gamma) S + (K E)^T W
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) X = mfma4(-(kv[sidx] * Dp[sidx]), S[sidx], X);
+    f4 W = {0.f, 0.f, 0.f, 0.f}, O = W;
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) W = mfma4(L.m[0][i16][4 * g + sidx], X[sidx], W);
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      O = mfma4(qv[sidx] * Dp[sidx], S[sidx], O);
+      O = mfma4(L.m[1][i16][4 * g + sidx], W[sidx], O);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      if (r < n) A.t.o[base + (size_t)r * hs + i16] = (uint16_t)(pack_bf2(O[e], 0.f) & 0xffffu);
+    }
+    f4 Sn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Sn[e] = S[e] * __shfl(Dp[e], 16 * g + 15);   // gamma of row 4 g + e
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) Sn = mfma4(L.m[2][4 * g + sidx][i16], W[sidx], Sn);
+    S = Sn;
+
+    const int done = t0 + n;
+    if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
+      const int dst = A.ckpt_slot[ck++];
+      if (dst >= 0 && dst < P.num_slots) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P.state[dst * per + hoff + (4 * g + e) * SD + i16] = S[e];
+        if (l == 0 && h == 0) {
+          kda_slot_meta mm{pos0 + done, 0, 0, 0, 0};
+          P.meta[dst] = mm;
+        }
+      }
+    }
+  }
+  const int out = A.out_slot[si];
+  if (out >= 0 && out < P.num_slots) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) P.state[out * per + hoff + (4 * g + e) * SD + i16] = S[e];
+    if (l == 0 && h == 0) {
+      kda_slot_meta mm{pos0 + len, 0, 0, 0, 0};
+      P.meta[out] = mm;
+    }
+  }
+}
+
 int device_cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -1065,8 +1277,12 @@ size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_ch
 }
 
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
-  if (p.dk != PD || a.chunk != PC) return launch_prefill_recurrent(p, a, s);
   if (a.n_seq <= 0) return hipSuccess;
+  if (p.dk == SD && a.chunk == SC) {
+    hipLaunchKernelGGL(prefill_small_kernel, dim3((unsigned)(a.n_seq * p.H)), dim3(64), 0, s, p, a);
+    return hipGetLastError();
+  }
+  if (p.dk != PD || a.chunk != PC) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(a.workspace);
   int32_t* choff = reinterpret_cast<int32_t*>(ws);
   int32_t* ckoff = choff + (a.n_seq + 1);

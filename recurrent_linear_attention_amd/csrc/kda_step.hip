@@ -516,74 +516,6 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void commit_direct_kernel(PoolView 
   }
 }
 
-// Recurrent-form prefill: one work-group per (sequence, head, value slice) walks its
-// sequence token by token with the decode step, exporting the state at every checkpoint
-// boundary inside the same pass and the final state at the end.
-template <int D>
-__global__ __launch_bounds__(StepCfg<D>::NT) void prefill_recurrent_kernel(PoolView P, PrefillLaunch A) {
-  using C = StepCfg<D>;
-  __shared__ StepLds<C> lds;
-  constexpr int NVS = D / C::VS;
-  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, si = blockIdx.x / (NVS * P.H);
-  const int t = threadIdx.x, cg = t % C::TPR, rg = t / C::TPR;
-  const int r0 = rg * C::RPT, c0 = vs * C::VS + cg * 4;
-  const int lo = A.cu_seqlens[si], hi = A.cu_seqlens[si + 1];
-  int ck = 0;   // first checkpoint entry of this sequence
-  if (A.ckpt_interval > 0)
-    for (int j = 0; j < si; ++j) ck += (A.cu_seqlens[j + 1] - A.cu_seqlens[j]) / A.ckpt_interval;
-  const int init = A.init_slot ? A.init_slot[si] : -1;
-  const int out = A.out_slot[si];
-  const size_t per = (size_t)P.H * D * D, hoff = (size_t)h * D * D;
-  float S[C::RPT][4];
-  if (init >= 0 && init < P.num_slots) {
-    load_state<C>(S, P.state + init * per + hoff, r0, c0);
-  } else {
-#pragma unroll
-    for (int r = 0; r < C::RPT; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S[r][c] = 0.f;
-  }
-  const int64_t pos0 = (init >= 0 && init < P.num_slots) ? P.meta[init].pos : 0;
-  auto fetch = [&](StepRaw<C>& r, int tok) {
-    const size_t row = (size_t)tok * P.H + h;
-    fetch_in<C, true>(r, A.t.q + row * D, A.t.k + row * D, A.t.v + row * D, A.t.a + row * D,
-                      A.t.b + row, r0, c0);
-  };
-  StepRaw<C> nxt;
-  if (lo < hi) fetch(nxt, lo);
-  state_ready<C>(S);
-  for (int tok = lo; tok < hi; ++tok) {
-    const size_t row = (size_t)tok * P.H + h;
-    StepIn<C> in;
-    unpack_in<C, true>(in, nxt);
-    if (tok + 1 < hi) fetch(nxt, tok + 1);
-    float o[4];
-    step<C, true>(S, in, lds, tok & 1, o);
-    if (rg == 0) {
-      uint32_t ow[2] = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
-      store_bf16_raw<4>(A.t.o + row * D + c0, ow);
-    }
-    const int done = tok + 1 - lo;
-    if (A.ckpt_interval > 0 && done % A.ckpt_interval == 0) {
-      const int dst = A.ckpt_slot[ck++];
-      if (dst >= 0 && dst < P.num_slots) {
-        store_state<C>(S, P.state + dst * per + hoff, r0, c0);
-        if (t == 0 && h == 0 && vs == 0) {
-          kda_slot_meta m{pos0 + done, 0, 0, 0, 0};
-          P.meta[dst] = m;
-        }
-      }
-    }
-  }
-  if (out >= 0 && out < P.num_slots) {
-    store_state<C>(S, P.state + out * per + hoff, r0, c0);
-    if (t == 0 && h == 0 && vs == 0) {
-      kda_slot_meta m{pos0 + (hi - lo), 0, 0, 0, 0};
-      P.meta[out] = m;
-    }
-  }
-}
-
 __global__ void rollback_kernel(PoolView P, int B, const int32_t* __restrict__ slots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B) return;
@@ -665,16 +597,6 @@ hipError_t launch_commit_direct(const PoolView& p, int32_t B, const int32_t* d_s
   else
     hipLaunchKernelGGL(commit_direct_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p,
                        d_slots, d_n_acc, draft, n_pos);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_recurrent(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
-  if (p.dk == 128)
-    hipLaunchKernelGGL(prefill_recurrent_kernel<128>, dim3(a.n_seq * p.H * (128 / StepCfg<128>::VS)),
-                       dim3(StepCfg<128>::NT), 0, s, p, a);
-  else
-    hipLaunchKernelGGL(prefill_recurrent_kernel<16>, dim3(a.n_seq * p.H * (16 / StepCfg<16>::VS)),
-                       dim3(StepCfg<16>::NT), 0, s, p, a);
   return hipGetLastError();
 }
 

@@ -213,7 +213,7 @@ def test_prefill_workspace_size_and_checks():
     p = HostPool(H=4, d=128)
     s = [p.alloc()[1] for _ in range(3)]
     p16 = HostPool(H=4, d=16)
-    # the token-by-token shape takes no workspace, nor does an empty call
+    # the d = 16 form keeps its chunks on chip and takes no workspace, nor does an empty call
     assert lib.kda_prefill_workspace_bytes(p16.h, 1000, 3, 16, 0) == 0
     assert lib.kda_prefill_workspace_bytes(p.h, 1000, 0, 64, 0) == 0
     # at most floor(1000 / 64) + 3 = 18 chunks, 61,952 bytes per (chunk, head), plus a small plan

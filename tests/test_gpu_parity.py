@@ -299,25 +299,29 @@ def test_rule_invariants_at_full_size():
     assert device_errors(g) == 0
 
 
+@pytest.mark.parametrize("d", [128, 16])
 @pytest.mark.parametrize("case", ["channels", "heads"])
-def test_prefill_strong_decay_matches_oracle(case):
+def test_prefill_strong_decay_matches_oracle(case, d):
     """Key channels that decay fast within a 16-token block take the exact fp32 path of the
     diagonal blocks: a = 0.3, 0.05 and 1e-3 on a few channels of three heads, and 1e-3 on one
     channel for 40 tokens mid-sequence ("channels"), or on every channel of a head ("heads");
     a = 0.6 sits just inside the fp16 factorisation (16-token decay 2.8e-4 >= 2^-12). Outputs,
     checkpoints and final states against the oracle (no NaN can pass), with a resumed sequence;
-    the informational flag is raised and reading the error word clears it."""
-    H, d, interval = 4, 128, 128
+    the informational flag is raised and reading the error word clears it. At d = 16 (chunk
+    16, fp32 factors) the exact path starts below a chunk decay of 2^-60: a = 0.3 stays on the
+    factored path there, 0.05 and 1e-3 take the exact one."""
+    H, interval = 4, 128
     lengths = [300, 130, 64]
-    rng = np.random.default_rng(960 + len(case))
+    rng = np.random.default_rng(960 + len(case) + d)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    ch = ([9, 50], [5, 77], [0, 64, 127], [3, 100], 20) if d == 128 else ([3, 9], [5, 12], [0, 7, 15], [3, 10], 2)
     if case == "channels":
-        tok.a[:, 0, [9, 50]] = 0.6
-        tok.a[:, 1, [5, 77]] = 0.3
-        tok.a[:, 2, [0, 64, 127]] = 0.05
-        tok.a[:, 3, [3, 100]] = 1e-3
-        tok.a[100:140, 0, 20] = 1e-3
+        tok.a[:, 0, ch[0]] = 0.6
+        tok.a[:, 1, ch[1]] = 0.3
+        tok.a[:, 2, ch[2]] = 0.05
+        tok.a[:, 3, ch[3]] = 1e-3
+        tok.a[100:140, 0, ch[4]] = 1e-3
     else:
         tok.a[:, 0, :] = 0.6
         tok.a[:, 1, :] = 0.3
@@ -340,16 +344,17 @@ def test_prefill_strong_decay_matches_oracle(case):
     assert g.kda_read_device_error() == 0
 
 
-def test_prefill_unit_key_readout_through_chunks():
+@pytest.mark.parametrize("d", [128, 16])
+def test_prefill_unit_key_readout_through_chunks(d):
     """The readout invariant of the rule through the chunked prefill: with a = 1, b = 1 and a
     unit key, k_t^T S_t = v_t^T after every token whatever the state was, so a query equal to
     the key reads o_t = v_t. Keys repeat from a small set of unit vectors that bf16 holds
     exactly (one-hot, or +-1/2 on four channels), across several chunks and a ragged tail, from
     a random initial state; outputs against v itself and against the oracle, states against the
     oracle."""
-    H, d = 4, 128
+    H = 4
     lengths = [200, 64, 37]
-    rng = np.random.default_rng(961)
+    rng = np.random.default_rng(961 + d)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     N = int(cu[-1])
     tok = ki.draw_tokens(rng, (N,), H, d, d)
@@ -1007,7 +1012,7 @@ def test_mixed_batch_commits_previous_verify(d):
     """Two serving steps: the second mixed batch commits the first one's verified drafts (its
     commit part) before verifying the same slots again, next to a new prefill and decodes.
     Every output, state and metadata entry against the oracle applying the same operations in
-    order. At d = 16 the prefill part is the token-recurrent kernel (chunk 16)."""
+    order, at d = 128 (chunk 64) and d = 16 (chunk 16)."""
     H, P = 4, 5
     g, o = pools(32, H, d)
     rng = np.random.default_rng(90)
