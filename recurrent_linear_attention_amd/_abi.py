@@ -14,7 +14,10 @@ from ctypes import POINTER, c_char_p, c_int32, c_size_t, c_uint32, c_void_p
 # HIP/HSA runtime (two runtimes in one process do not share devices, streams or memory).
 import torch  # noqa: F401
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkda.so")
+# KDA_LIB_PATH names another build of the same library (the tests load a host-only build under
+# the address and undefined-behaviour sanitizers through it).
+LIB_PATH = os.environ.get("KDA_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libkda.so")
 
 KDA_OK, KDA_EINVAL, KDA_ENOSLOT, KDA_ESTATE, KDA_EUNSUPPORTED, KDA_EWORKSPACE, KDA_EHIP = \
     0, -1, -2, -3, -4, -5, -6

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libkda.so")
 
-SOURCES = ["kda_pool.cpp", "kda_step.hip", "kda_prefill.hip"]
+SOURCES = ["kda_pool.cpp", "kda_plan.cpp", "kda_step.hip", "kda_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -27,6 +27,14 @@ struct StepTensors {
   uint16_t* o;
 };
 
+// Geometry of the chunked prefill at d = 128, shared by the kernels and the host plan: head
+// dim, chunk, bytes of one (chunk, head) operand block in the workspace, and the largest batch
+// whose plan the operand kernel computes itself.
+constexpr int PREFILL_D = 128;
+constexpr int PREFILL_CHUNK = 64;
+constexpr int PREFILL_BLOCK_BYTES = 60 * 1024 + 4 * PREFILL_D;
+constexpr int PREFILL_PLAN_INLINE_MAX = 64;
+
 // Width plan of the prefill's sequential pass: the sequences ranked rank_end[g - 1] ..
 // rank_end[g] - 1 by length (rank_end[-1] = 0) run in work-groups of vsw[g] value columns
 // (16, 32, 64 or 128), work-groups wg_begin[g] .. wg_begin[g + 1] - 1 (each group a multiple of
@@ -74,8 +82,10 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
 // latency / CU-time model of the pass; beyond 64 sequences one width for all.
 StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H);
 // Device workspace the prefill of n_seq sequences with n_chunks chunks in total needs (0 for
-// d = 16, whose chunked form keeps every chunk on chip).
+// d = 16, whose chunked form keeps every chunk on chip): the plan arrays, then the operand
+// blocks.
 size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks);
+size_t prefill_plan_bytes(int n_seq);
 // Scratch of the allocation-free prefill: a file-scope device array of this many bytes in the
 // prefill's code object; prefill_scratch returns its address on the current device (looked up
 // once per device).

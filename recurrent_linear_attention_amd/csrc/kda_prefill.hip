@@ -55,8 +55,8 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-constexpr int PD = 128;           // head dim (dk = dv)
-constexpr int PC = 64;            // chunk
+constexpr int PD = PREFILL_D;     // head dim (dk = dv)
+constexpr int PC = PREFILL_CHUNK; // chunk
 constexpr int PNB = PC / 16;      // 16-row blocks per chunk
 constexpr int NPAIR = PNB * (PNB + 1) / 2;
 constexpr int P16 = PD + 8;       // row pitch (halves) of [.][PD] fp16 arrays
@@ -78,6 +78,7 @@ constexpr int OFF_T = 48 * FRAG;      // T:      f = tri_frag(rt, kk), token blo
 constexpr int OFF_AQ = 54 * FRAG;     // A_qk:   same
 constexpr int OFF_GAM = 60 * FRAG;    // 2^(G_C), fp32 [PD]
 constexpr int BLOCK_BYTES = 60 * FRAG + 4 * PD;   // 61952, a multiple of 256
+static_assert(BLOCK_BYTES == PREFILL_BLOCK_BYTES, "operand block size shared with the host plan");
 
 // Lower-triangular 64x64 operands keep only the fragments with kk <= rt / 2:
 // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prefill_plan_kernel(const int32_
 // A batch of at most 64 sequences is planned inside chunk_prep_kernel instead (one lane per
 // sequence), which saves the plan kernel's launch: lane i gets sequence i's length, chunk count
 // and exclusive chunk / checkpoint offsets.
-constexpr int PLAN_INLINE_MAX = 64;
+constexpr int PLAN_INLINE_MAX = PREFILL_PLAN_INLINE_MAX;
 struct LanePlan {
   int len, nch, choff, ckoff, n_ck;
 };
@@ -1217,21 +1218,6 @@ __global__ __launch_bounds__(64) void prefill_small_kernel(PoolView P, PrefillLa
   }
 }
 
-int device_cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-size_t plan_bytes(int n_seq) { return align256(sizeof(int32_t) * (3 * (size_t)n_seq + 1)); }
 
 hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t* choff,
                         const int32_t* ckoff, const int32_t* order, const char* blocks, hipStream_t s) {
@@ -1271,11 +1257,6 @@ hipError_t prefill_scratch(void** out) {
   return hipSuccess;
 }
 
-size_t prefill_workspace_bytes(int dk, int chunk, int H, int n_seq, int64_t n_chunks) {
-  if (dk != PD || chunk != PC || n_seq <= 0) return 0;
-  return plan_bytes(n_seq) + (size_t)n_chunks * H * BLOCK_BYTES;
-}
-
 hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t s) {
   if (a.n_seq <= 0) return hipSuccess;
   if (p.dk == SD && a.chunk == SC) {
@@ -1287,7 +1268,7 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
   int32_t* choff = reinterpret_cast<int32_t*>(ws);
   int32_t* ckoff = choff + (a.n_seq + 1);
   int32_t* order = ckoff + a.n_seq;
-  char* blocks = ws + plan_bytes(a.n_seq);
+  char* blocks = ws + prefill_plan_bytes(a.n_seq);
   hipError_t e = hipSuccess;
   if (a.n_seq > PLAN_INLINE_MAX || a.n_chunks == 0) {
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a.cu_seqlens, a.n_seq,
@@ -1302,90 +1283,6 @@ hipError_t launch_prefill(const PoolView& p, const PrefillLaunch& a, hipStream_t
     if (e != hipSuccess) return e;
   }
   return launch_state(p, a, choff, ckoff, order, blocks, s);
-}
-
-StatePlan plan_state_pass(const int32_t* h_cu, int n_seq, int H) {
-  // Per-chunk latency of one chain (us) with 16, 32, 64 and 128 value columns per work-group,
-  // measured on MI355X for the mixed 16384-token batch, plus a work-group's start-up; the pass
-  // keeps one work-group per CU, and list scheduling in rank order packs CU-time to ~85%.
-  constexpr float LAT[4] = {1.55f, 1.8f, 2.3f, 3.1f};
-  constexpr float START = 3.f, PACK = 0.85f;
-  constexpr int WIDTH[4] = {16, 32, 64, 128};
-  const int cus = device_cu_count();
-  auto build = [&](int n_groups, const int* ends, const int* widths) {
-    StatePlan sp{};
-    sp.n_groups = n_groups;
-    int begin = 0, r0 = 0;
-    for (int g = 0; g < n_groups; ++g) {
-      sp.rank_end[g] = ends[g];
-      sp.vsw[g] = widths[g];
-      sp.wg_begin[g] = begin;
-      begin += ((ends[g] - r0) * H + 7) / 8 * 8 * (PD / widths[g]);
-      r0 = ends[g];
-    }
-    sp.wg_begin[n_groups] = begin;
-    return sp;
-  };
-  // one width for all: the narrowest whose grid fits in one round of CUs, else 64 columns
-  const int n_hg = n_seq * H;
-  const int wu = n_hg * 8 <= cus ? 0 : (n_hg * 4 <= cus ? 1 : 2);
-  const int end_all[1] = {n_seq}, w_all[1] = {WIDTH[wu]};
-  const StatePlan uniform = build(1, end_all, w_all);
-  if (n_seq < 2 || n_seq > PLAN_INLINE_MAX) return uniform;
-  // chunk counts in rank order: descending length, ties lower index first (the plan's order)
-  int idx[PLAN_INLINE_MAX], nch[PLAN_INLINE_MAX];
-  for (int i = 0; i < n_seq; ++i) idx[i] = i;
-  auto len = [&](int i) { return h_cu[i + 1] - h_cu[i]; };
-  std::stable_sort(idx, idx + n_seq, [&](int x, int y) { return len(x) > len(y); });
-  for (int r = 0; r < n_seq; ++r) nch[r] = seq_chunks(len(idx[r]), PC, 0);
-  auto predict = [&](const int* wi) {
-    float chain = 0.f, cu_time = 0.f;
-    int64_t wgs = 0;
-    for (int r = 0; r < n_seq; ++r) {
-      const float t = nch[r] * LAT[wi[r]] + START;
-      const int slices = PD / WIDTH[wi[r]];
-      chain = std::max(chain, t);
-      cu_time += (float)H * slices * t;
-      wgs += (int64_t)H * slices;
-    }
-    return wgs <= cus ? chain : std::max(chain, cu_time / (PACK * cus));
-  };
-  int wi[PLAN_INLINE_MAX], best[PLAN_INLINE_MAX];
-  for (int r = 0; r < n_seq; ++r) wi[r] = wu;
-  const float t_uniform = predict(wi);
-  float t_best = t_uniform;
-  bool found = false;
-  // each candidate bounds every chain by one chain's time at one width; each rank then takes
-  // the widest slices that stay within it (non-decreasing along the ranks)
-  for (int rr = 0; rr < n_seq; ++rr)
-    for (int ww = 0; ww < 4; ++ww) {
-      const float bound = nch[rr] * LAT[ww] + START;
-      bool ok = true;
-      for (int r = 0; r < n_seq && ok; ++r) {
-        int w = 3;
-        while (w >= 0 && nch[r] * LAT[w] + START > bound) --w;
-        if (w < 0) ok = false;
-        wi[r] = w;
-      }
-      if (!ok) continue;
-      const float t = predict(wi);
-      if (t < t_best) {
-        t_best = t;
-        found = true;
-        std::copy(wi, wi + n_seq, best);
-      }
-    }
-  // a different plan only for a clear predicted gain (the model is coarse)
-  if (!found || t_best > 0.95f * t_uniform) return uniform;
-  int ends[4], widths[4], n_groups = 0;
-  for (int r = 0; r < n_seq; ++r) {
-    if (n_groups == 0 || WIDTH[best[r]] != widths[n_groups - 1]) {
-      if (n_groups == 4) return uniform;
-      widths[n_groups++] = WIDTH[best[r]];
-    }
-    ends[n_groups - 1] = r + 1;
-  }
-  return build(n_groups, ends, widths);
 }
 
 }  // namespace kda
