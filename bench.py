@@ -1,17 +1,30 @@
-"""Benchmark: one serving step of the KDA engine on the mixed 16384-token batch.
+"""Benchmark: one serving step of the KDA engine on the mixed 16384-token batch, plus the
+single-purpose workloads the per-kernel targets are quoted on.
 
 A step is the whole hot path over one packed batch -- 6 chunked prefills (lognormal lengths,
 16316 tokens), 32 single-token decodes, the ReplaySSM commit of the 4 sequences verified in the
 previous step and 4 speculative verifies of 1+8 positions on them, all issued by one
-kda_mixed_batch call -- on H=32 heads
-(one GPU's share), d_k = d_v = 128, a pool of 512 fp32 state slots. Inputs are synthetic and
-seeded (kda_inputs.mixed_workload) and resident in HBM before timing starts.
+kda_mixed_batch call -- on H=32 heads (one GPU's share), d_k = d_v = 128, a pool of 512 fp32
+state slots. Inputs are synthetic and seeded (kda_inputs) and resident in HBM before timing
+starts. `value` = tokens per second of the whole step (16384 / step time, wall clock over the
+timed steps).
 
-Prints one JSON line. `value` = tokens per second of the whole step (16384 / step time).
-`roofline` describes the dominant part, the chunked prefill (one kda_prefill call: its
-chunk_prep and state_pass kernels), timed with HIP events on the stream the library launches
-on, in a second timed pass that issues the same calls one by one. `cpu_baseline` times the CPU
-oracle on a bounded sample (a subset of heads).
+`roofline` describes the dominant part of the step, the chunked prefill (one kda_prefill call:
+its chunk_prep and state_pass kernels), timed with HIP events on the stream the library
+launches on, in a second pass that issues the step's calls one by one (`kernels`).
+
+`configs` times each call on its own workload, cold: before every timed call a 512 MiB write
+evicts the 256 MB Infinity Cache, and a HIP event pair on the call's stream brackets the call
+alone (median and p10 / p90 over the iterations; `ms_warm` = back-to-back calls without the
+eviction, for contrast):
+  * decode_b16: 16 single-token decodes against a 256-slot pool (slots a random permutation);
+  * verify_commit_b4: 4 speculative verifies of 1+8 positions, then the ReplaySSM commit of
+    the accepted drafts (accepted counts ~ U{0..8});
+  * prefill_8192: one 8192-token prompt, chunk 64, the state exported to a checkpoint slot
+    every 1024 tokens inside the pass (8 checkpoints) and to the out slot.
+
+`cpu_baseline` runs the CPU oracle (fp64 numpy, test infrastructure) on the mixed step, split
+by heads over a process pool of the host's cores, before the GPU is touched.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 30]
 
@@ -32,24 +45,30 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA tokens/s + achieved HBM GB/s (decode/verify), MFMA % (prefill), 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16
+DTYPE = "bf16 q/k/v/o, fp16 matrix-core operands, fp32 state and accumulation"
 
 # Algorithmic bytes (d = 128, fp32 state, bf16 q/k/v/o, fp32 a and b).
 D = 128
+C = 64
 STATE_B = D * D * 4
 TOK_IN_B = 3 * D * 2 + D * 4 + 4            # q, k, v bf16 + a fp32 + b fp32
 TOK_OUT_B = D * 2                           # o bf16
 RING_ENTRY_B = 2 * D * 2 + D * 4 + 4        # k, v bf16 + a fp32 + b fp32
-
+# Algorithmic flops of the chunked prefill per token-head (triangle-exact): three d x d state
+# contractions (6 d^2), the intra-chunk products C (3 d_k + 2 d_v) and the triangular solve
+# C^2 / 3. (The kernels need C (2 d_k + 2 d_v) of the middle term: they form W = T (V - Kt S)
+# in one triangular product instead of T V and T Kt separately.)
+PREFILL_FLOP_TOK_HEAD = 6 * D * D + C * (3 * D + 2 * D) + C * C / 3
 
 # HBM traffic of one prefill call of the mixed step (its two kernels: chunk_prep, which plans a
-# batch of this size itself, and state_pass), from rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch)
-# scaled by the counters' reading for a 1 GiB device copy (FETCH_SIZE reads half the copied
-# bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid only for the kernel source it was
-# measured on (first 16 hex digits of its SHA-256); for any other source the bench reports
-# traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "4d34be1df2b4e43e", "fetch_scale": 2.0, "write_scale": 1.0,
-                   "fetch_kib": {"chunk_prep_kernel": 269326, "state_pass_kernel": 316202},
-                   "write_kib": {"chunk_prep_kernel": 501492, "state_pass_kernel": 142817}}
+# batch of this size itself, and state_pass), from rocprofv3 counter passes (FETCH_SIZE and
+# WRITE_SIZE, KiB per dispatch) scaled by the counters' reading for a 1 GiB device copy
+# (FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid
+# only for the kernel source it was measured on (first 16 hex digits of its SHA-256); for any
+# other source the bench reports traffic as null.
+PREFILL_TRAFFIC = {"source_sha256_16": "9936c75a2d308404", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"chunk_prep_kernel": 269336, "state_pass_kernel": 316197},
+                   "write_kib": {"chunk_prep_kernel": 501505, "state_pass_kernel": 142817}}
 
 
 def prefill_traffic_bytes():
@@ -67,10 +86,8 @@ def prefill_bytes(n_tok, H, n_out, n_init=0, n_ckpt=0):
     return n_tok * H * (TOK_IN_B + TOK_OUT_B) + (n_out + n_init + n_ckpt) * H * STATE_B
 
 
-def prefill_flops(n_tok, H, C=64):
-    # chunked form, triangle-exact: three d x d state contractions per token (K~S, Q~S,
-    # Kbar^T W), four C x C x d triangular products per chunk, the triangular solve.
-    return n_tok * H * (6 * D * D + 4 * D * C + C * C / 3)
+def prefill_flops(n_tok, H):
+    return n_tok * H * PREFILL_FLOP_TOK_HEAD
 
 
 def decode_bytes(B, H):
@@ -95,26 +112,25 @@ def commit_bytes(n_replayed_total, B, H):
     return B * H * 2 * STATE_B + n_replayed_total * H * RING_ENTRY_B
 
 
-def cpu_baseline(w, heads: int):
-    """The CPU oracle as it stands, on the same workload restricted to `heads` heads."""
+# ----------------------------------------------------------------------------- CPU baseline
+
+_CPU_W = None   # the mixed workload as numpy arrays, set in the parent before the workers fork
+
+
+def _oracle_step_on_heads(heads):
+    """Worker: the CPU oracle on the whole mixed step restricted to `heads` (one thread)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import KDAPool as OPool
-    H = w["H"]
-    hs = list(range(heads))
-    tok = w["tokens"]
-
-    def sub(x):
-        return x[:, hs] if x.ndim == 2 else x[:, hs, :]
-
-    npd = {n: sub(x) for n, x in tok.np.items()}
-    o = OPool(w["n_slots"], heads, D, D, w["ring_cap"])
+    w = _CPU_W
+    hs = list(heads)
+    npd = {n: (x[:, hs] if x.ndim == 2 else x[:, hs, :]) for n, x in w["tokens"].items()}
+    o = OPool(w["n_slots"], len(hs), D, D, w["ring_cap"])
     for _ in range(w["n_slots"]):
         o.alloc()
     ds, vs, ps = w["decode_slots"], w["verify_slots"], w["prefill_slots"]
-    st = w["states"].double().numpy()[:, hs]
-    o.state[np.concatenate([ds, vs])] = st
+    o.state[np.concatenate([ds, vs])] = w["states"][:, hs]
     n_pre, nd, P = w["cu_seqlens"][-1], w["n_decode"], w["n_pos"]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -124,13 +140,222 @@ def cpu_baseline(w, heads: int):
         o.verify({n: x[n_pre + nd:].reshape((len(vs), P) + x.shape[1:]) for n, x in npd.items()},
                  vs)
         o.commit(vs, w["n_accepted"])
-        dt = time.perf_counter() - t0
-    total_tok = int(w["cu_seqlens"][-1]) + nd + len(vs) * P
-    return {"value": total_tok * heads / H / dt, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the whole mixed step (prefill, decode, verify, commit) on {heads} of "
-                      f"{H} heads, fp64 numpy, one thread; {dt:.1f} s of CPU time, scaled "
-                      f"to all {H} heads"}
+        return time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, max_workers: int):
+    """The CPU oracle as it stands (fp64 numpy), on the whole mixed step with all heads: the
+    (sequence, head) chains are independent, so the heads are split over a pool of worker
+    processes, one thread each, one per host core the process may run on (at most
+    max_workers). Must run before the GPU is initialised: the workers are forked, and they
+    get plain numpy arrays only (torch's thread pools do not survive a fork)."""
+    import multiprocessing as mp
+    global _CPU_W
+    _CPU_W = {**{k: w[k] for k in ("n_slots", "ring_cap", "decode_slots", "verify_slots",
+                                   "prefill_slots", "cu_seqlens", "n_decode", "n_pos",
+                                   "n_accepted")},
+              "tokens": w["tokens"].np, "states": w["states"].double().numpy()}
+    H = w["H"]
+    n = max(1, min(len(os.sched_getaffinity(0)), max_workers, H))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    parts = [list(range(i, H, n)) for i in range(n)]
+    with mp.get_context("fork").Pool(n) as pool:
+        pool.map(_oracle_step_on_heads, [[0]] * n)          # workers up, modules imported
+        t0 = time.perf_counter()
+        per = pool.map(_oracle_step_on_heads, parts)
+        wall = time.perf_counter() - t0
+    total_tok = int(w["cu_seqlens"][-1]) + w["n_decode"] + w["n_verify"] * w["n_pos"]
+    return {"value": round(total_tok / wall, 1), "unit": "tokens/s", "cores": n,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"the whole mixed step (6 prefills, {w['n_decode']} decodes, "
+                      f"{w['n_verify']} verifies of 1+{w['n_pos'] - 1}, their commit) on all "
+                      f"{H} heads, fp64 numpy, heads split over {n} worker processes (one "
+                      f"thread each); wall {wall:.2f} s, {sum(per):.1f} s of CPU time"}
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+def _stats(ms):
+    import numpy as np
+    a = np.asarray(ms)
+    return {"ms": round(float(np.median(a)), 5), "ms_p10": round(float(np.percentile(a, 10)), 5),
+            "ms_p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def _bw(bytes_, ms):
+    gbs = bytes_ / ms / 1e6
+    return {"alg_bytes": int(bytes_), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+class Cold:
+    """Times calls cold: a 512 MiB write (untimed, same stream) evicts the 256 MB Infinity
+    Cache before each timed call; an event pair on the stream brackets the call alone."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.scratch = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def evict(self):
+        self.n += 1
+        self.scratch.fill_(float(self.n))
+
+    def time(self, iters, calls):
+        """calls: functions run in order each iteration, each timed cold. Returns per-call lists
+        of event times (ms)."""
+        torch = self.torch
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in calls] for _ in range(iters)]
+        for it in range(iters):
+            for j, fn in enumerate(calls):
+                self.evict()
+                ev[it][j][0].record()
+                fn()
+                ev[it][j][1].record()
+        torch.cuda.synchronize()
+        return [[ev[it][j][0].elapsed_time(ev[it][j][1]) for it in range(iters)] for j in range(len(calls))]
+
+    def warm(self, iters, fn):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+
+def measured_peaks(torch, dev):
+    """What this GPU sustains on plain work, beside the published peaks: a 1 GiB device-to-device
+    copy (bytes read + written per second) and a 8192^3 bf16 matmul (dense TFLOP/s), each the
+    best of 5 timed repeats after a warm-up."""
+    src = torch.ones(2**28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    ms_copy = best(lambda: dst.copy_(src))
+    ms_mm = best(lambda: torch.matmul(a, b))
+    res = {"hbm_spec_GBps": HBM_PEAK_GBS, "mfma_fp16_spec_TFLOPs": MFMA_PEAK_TFLOPS,
+           "copy_GBps": round(2 * src.numel() * 4 / ms_copy / 1e6, 1),
+           "matmul_bf16_TFLOPs": round(2 * 8192**3 / ms_mm / 1e9, 1)}
+    del src, dst, a, b
+    return res
+
+
+def bench_decode(torch, kda, ki, dev, cold, iters):
+    w = ki.decode_workload(1)
+    H, B = w["H"], w["B"]
+    pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+    for _ in range(w["n_slots"]):
+        pool.kda_slot_alloc()
+    slots = kda.IndexArray(w["slots"], dev)
+    pool.state[w["slots"].tolist()] = w["states"].to(dev)
+    t = w["tokens"]
+    q, k, v, a, b = (x.to(dev).contiguous() for x in (t.q, t.k, t.v, t.a, t.b))
+    o = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    call = lambda: pool.kda_decode(q, k, v, a, b, slots, o=o)  # noqa: E731
+    for _ in range(5):
+        call()
+    (ms,) = cold.time(iters, [call])
+    st = _stats(ms)
+    out = {"workload": f"decode: B={B} sequences x 1 token, H={H}, d={D}, pool {w['n_slots']} "
+                       "slots (random permutation), fp32 state", **st,
+           **_bw(decode_bytes(B, H), st["ms"]), "tokens_per_s": round(B / (st["ms"] / 1e3), 1),
+           "ms_warm": round(cold.warm(iters, call), 5)}
+    del pool
+    return out
+
+
+def bench_verify_commit(torch, kda, ki, dev, cold, iters):
+    import numpy as np
+    w = ki.verify_workload(2)
+    H, B, P = w["H"], w["B"], w["n_pos"]
+    pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+    for _ in range(w["n_slots"]):
+        pool.kda_slot_alloc()
+    slots = kda.IndexArray(w["slots"], dev)
+    pool.state[w["slots"].tolist()] = w["states"].to(dev)
+    t = w["tokens"]
+    q, k, v, a, b = (x.to(dev).contiguous() for x in (t.q, t.k, t.v, t.a, t.b))
+    o = torch.empty((B, P, H, D), dtype=torch.bfloat16, device=dev)
+    na = torch.from_numpy(w["n_accepted"]).to(dev)
+    ver = lambda: pool.kda_verify(q, k, v, a, b, slots, o=o)  # noqa: E731
+    com = lambda: pool.kda_commit(slots, na)  # noqa: E731
+    for _ in range(3):
+        ver()
+        com()
+    ms_v, ms_c = cold.time(iters, [ver, com])
+    sv, sc = _stats(ms_v), _stats(ms_c)
+    n_rep = int(np.sum(1 + w["n_accepted"]))
+    out = {"workload": f"speculative verify of B={B} x 1+{P - 1} positions, then ReplaySSM commit "
+                       f"of accepted counts {w['n_accepted'].tolist()} ({n_rep} positions "
+                       f"replayed), H={H}, d={D}, pool {w['n_slots']} slots, ring of {w['ring_cap']}",
+           "verify": {**sv, **_bw(verify_bytes(B, P, H), sv["ms"]),
+                      "positions_per_s": round(B * P / (sv["ms"] / 1e3), 1)},
+           "commit": {**sc, **_bw(commit_bytes(n_rep, B, H), sc["ms"])},
+           "committed_tokens_per_s": round(n_rep / ((sv["ms"] + sc["ms"]) / 1e3), 1)}
+    del pool
+    return out
+
+
+def bench_prefill(torch, kda, ki, dev, cold, iters):
+    w = ki.prefill_workload(3)
+    H, L, I = w["H"], w["cu_seqlens"][-1], w["ckpt_interval"]
+    n_ck = L // I
+    pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+    for _ in range(w["n_slots"]):
+        pool.kda_slot_alloc()
+    t = w["tokens"]
+    q, k, v, a, b = (x.to(dev).contiguous() for x in (t.q, t.k, t.v, t.a, t.b))
+    o = torch.empty((L, H, D), dtype=torch.bfloat16, device=dev)
+    cu, out = kda.IndexArray(w["cu_seqlens"], dev), kda.IndexArray([0], dev)
+    cks = kda.IndexArray(list(range(1, 1 + n_ck)), dev)
+    call = lambda: pool.kda_prefill(q, k, v, a, b, cu, out, ckpt_slots=cks, ckpt_interval=I, o=o)  # noqa: E731
+    for _ in range(3):
+        call()
+    (ms,) = cold.time(iters, [call])
+    st = _stats(ms)
+    byts, fl = prefill_bytes(L, H, n_out=1, n_ckpt=n_ck), prefill_flops(L, H)
+    bw = _bw(byts, st["ms"])
+    tf = fl / st["ms"] / 1e9
+    res = {"workload": f"prefill: one {L}-token prompt, H={H}, d={D}, chunk {C}, state checkpoint "
+                       f"every {I} tokens inside the pass ({n_ck} checkpoints) and at the end",
+           **st, **bw, "tokens_per_s": round(L / (st["ms"] / 1e3), 1),
+           "alg_flops": int(fl), "alg_TFLOPs": round(tf, 2), "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+           # the MFMA rate this workload would reach at full HBM bandwidth (arithmetic intensity x
+           # 8 TB/s) and the achieved share of it, which equals hbm_frac
+           "hbm_bound_TFLOPs": round(fl / byts * HBM_PEAK_GBS / 1e3, 1),
+           "frac_of_hbm_bound_ceiling": bw["hbm_frac"],
+           "ms_warm": round(cold.warm(max(iters // 2, 1), call), 5)}
+    del pool
+    return res
 
 
 def main():
@@ -138,8 +363,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--config-iters", type=int, default=50,
+                    help="cold timed calls per single-purpose workload")
+    ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a known-size reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -161,13 +389,20 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
 
     import kda_inputs as ki
+
+    w = ki.mixed_workload(4)
+    cpu = None
+    if not args.no_cpu:   # before the GPU is touched: the oracle's workers are forked
+        print("bench: CPU oracle baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_workers)
+
+    import torch
+
     import recurrent_linear_attention_amd as kda
     from recurrent_linear_attention_amd import IndexArray
 
-    w = ki.mixed_workload(4)
     H, P = w["H"], w["n_pos"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -194,6 +429,7 @@ def main():
         pool.kda_mixed_batch(q, k, v, a, b, cu, i_ps, i_ds, i_vs, P, o=o, commit_slots=i_vs,
                              n_accepted=na)
 
+    print("bench: mixed step ...", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -242,9 +478,7 @@ def main():
     byts = {"prefill": prefill_bytes(n_pre, H, len(ps)), "decode": decode_bytes(nd, H),
             "verify": verify_bytes(nv, P, H), "commit": commit_bytes(n_rep, nv, H),
             "verify_direct": verify_direct_bytes(nv, P, H), "commit_direct": commit_direct_bytes(nv, H)}
-    kernels = {n: {"ms": round(ms[n], 5), "alg_bytes": byts[n],
-                   "GBps": round(byts[n] / ms[n] / 1e6, 1),
-                   "hbm_frac": round(byts[n] / ms[n] / 1e6 / HBM_PEAK_GBS, 4)} for n in names}
+    kernels = {n: {"ms": round(ms[n], 5), **_bw(byts[n], ms[n])} for n in names}
     pf = prefill_flops(n_pre, H)
     kernels["prefill"]["alg_TFLOPs"] = round(pf / ms["prefill"] / 1e9, 2)
     kernels["prefill"]["mfma_frac"] = round(pf / ms["prefill"] / 1e9 / MFMA_PEAK_TFLOPS, 4)
@@ -254,22 +488,36 @@ def main():
                 "kernel": "prefill: one kda_prefill call over all sequences of the batch "
                           "(chunk_prep and state_pass kernels, back to back on one stream)",
                 "alg_bytes_per_launch": byts["prefill"]}
+    del pool
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_heads)
+    configs = peaks = None
+    if not args.no_configs:
+        print("bench: single-purpose workloads (cold) ...", file=sys.stderr, flush=True)
+        cold = Cold(torch, dev)
+        configs = {"decode_b16": bench_decode(torch, kda, ki, dev, cold, args.config_iters),
+                   "verify_commit_b4": bench_verify_commit(torch, kda, ki, dev, cold, args.config_iters),
+                   "prefill_8192": bench_prefill(torch, kda, ki, dev, cold, max(args.config_iters // 2, 1))}
+        del cold
+        peaks = measured_peaks(torch, dev)
+        # each HBM-bound figure also as a share of what a plain device copy sustains
+        for part in (configs["decode_b16"], configs["verify_commit_b4"]["verify"],
+                     configs["verify_commit_b4"]["commit"], configs["prefill_8192"]):
+            part["copy_frac"] = round(part["GBps"] / peaks["copy_GBps"], 4)
+        for part in kernels.values():
+            part["copy_frac"] = round(part["GBps"] / peaks["copy_GBps"], 4)
 
     out = {"metric": METRIC, "value": round(total_tok / (ms_step / 1e3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 4), "ms_per_step_device": round(ms_step_dev, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-           "data": "synthetic (seeded, kda_inputs.mixed_workload)",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+           "data": "synthetic (seeded, kda_inputs)",
            "config": {"workload": "mixed varlen batch: 6 prefills (lognormal lengths "
                                   f"{w['lengths']}) + {nd} decodes + ReplaySSM commit of the "
                                   f"previous step's {nv} verifies + {nv} verifies of 1+{P - 1}",
                       "tokens_per_step": total_tok, "heads": H, "d_k": D, "d_v": D,
-                      "chunk": 64, "pool_slots": w["n_slots"]},
-           "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels}
+                      "chunk": C, "pool_slots": w["n_slots"]},
+           "roofline": roofline, "cpu_baseline": cpu, "peaks": peaks, "kernels": kernels,
+           "configs": configs}
     print(json.dumps(out), flush=True)
 
 
