@@ -642,22 +642,31 @@ struct StateFetch {
   static constexpr int N_KV = PART + SB::NV, N_QTA = PART + TRI;
   const char* bsrc;          // operand block of the chunk
   const uint16_t* vsrc;      // V[token 0 of the chunk][head][col0]
-  uint32_t buf, wb;          // LDS buffer, and its part for this wave
-  int n, hstr, t;
+  uint32_t buf;              // LDS buffer
+  int n, hstr, t, rot;
   __device__ __forceinline__ StateFetch(const char* blk0, const PrefillLaunch& A, int c, int H, int lo,
-                                        int len, int h, int col0, int t_, int w, uint32_t buf_)
+                                        int len, int h, int col0, int t_, uint32_t buf_)
       : bsrc(blk0 + (size_t)c * H * BLOCK_BYTES),
         buf(buf_),
-        wb((uint32_t)__builtin_amdgcn_readfirstlane((int)(buf_ + 16 * 64 * w))),
         hstr(H * PD),
-        t(t_) {
+        t(t_),
+        rot((col0 / VSW) * 128) {
     int t0;
     chunk_span(c, len, PC, A.ckpt_interval, &t0, &n);
     vsrc = A.t.v + (size_t)(lo + t0) * H * PD + (size_t)h * PD + col0;
   }
+  // Units t + NT j of a part of `count` units per thread, whole waves of 64 consecutive units
+  // per instruction. The slices of one head (which read the same block on one XCD at about the
+  // same time) start at different 2 KiB offsets of the part, spreading their requests over the
+  // L2 channels (2.5% on one 8192-token prompt at 16-column slices).
   __device__ __forceinline__ void units(int off, int count) const {
+    const int total = NT * count, sh = rot % total, l = t & 63;
 #pragma unroll
-    for (int j = 0; j < count; ++j) lds_dma16(bsrc + off + 16 * (t + NT * j), wb + off + 16 * NT * j);
+    for (int j = 0; j < count; ++j) {
+      int u0 = (t - l) + NT * j + sh;
+      if (u0 >= total) u0 -= total;
+      lds_dma16(bsrc + off + 16 * (u0 + l), (uint32_t)__builtin_amdgcn_readfirstlane((int)(buf + off + 16 * u0)));
+    }
   }
   __device__ __forceinline__ void kv() const {
     units(OFF_KT, PART);
@@ -744,7 +753,7 @@ __device__ __forceinline__ void state_pass_body(const PoolView& P, const Prefill
   const int64_t pos0 = has_init ? P.meta[init].pos : 0;
   const int nlast = nch - 1;
   auto sf = [&](int c) __attribute__((always_inline)) {   // past the last chunk: repeat it
-    return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, w, (c & 1) ? lds1 : lds0);
+    return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, (c & 1) ? lds1 : lds0);
   };
   if (loads) {
     // ---- load waves ------------------------------------------------------------------------

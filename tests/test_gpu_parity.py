@@ -170,14 +170,13 @@ def test_verify_commit_rollback_full_size():
 
 
 @pytest.mark.parametrize("d", [128, 16])
-@pytest.mark.parametrize("P", [1, 2, 3, 8, 9])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 9, 16, 17])
 def test_verify_commit_every_position_count(d, P):
     """Verify of P positions (odd counts end the kernels' two-position loop with a padding
     position, even ones do not), then commits accepting P - 1 and 0 drafts on two sequences:
-    outputs, ring entries and metadata against the oracle, nothing written by the padding
-    position, and the committed states bit-identical to the same positions applied as decode
-    calls."""
-    H, R = 4, 9
+    outputs, ring entries and metadata against the oracle, nothing written past the P entries,
+    and the committed states bit-identical to the same positions applied as decode calls."""
+    H, R = 4, max(9, P)
     rng = np.random.default_rng(700 + 10 * P + d)
     g, o = pools(8, H, d, R)
     slots = np.array([2, 5], dtype=np.int32)
@@ -211,6 +210,35 @@ def test_verify_commit_every_position_count(d, P):
         g2.kda_decode(*tj, slots[live])
     torch.cuda.synchronize()
     assert torch.equal(g2.state[slots.tolist()], g.state[slots.tolist()])
+    assert device_errors(g) == 0
+
+
+@pytest.mark.parametrize("P", [9, 16])
+def test_verify_under_strong_decay(P):
+    """Verify and commit with strongly decaying channels: a = 0.3, 1e-3 and 0 (a full forget of
+    the channel) at every position, outputs and committed states against the oracle."""
+    H, d = 4, 128
+    rng = np.random.default_rng(970 + P)
+    g, o = pools(8, H, d, max(9, P))
+    slots = np.array([1, 6], dtype=np.int32)
+    put_states(g, o, slots, ki.draw_states(rng, 2, H, d, d))
+    tok = ki.draw_tokens(rng, (2, P), H, d, d)
+    tok.a[:, :, 0, [3, 70]] = 0.3
+    tok.a[:, :, 1, [5, 9, 127]] = 1e-3
+    tok.a[:, :, 2, 64] = 0.0
+    tok.a[:, :, 3, :] = 1e-3
+    tok.np["a"] = tok.a.to(torch.float64).numpy()
+    O = g.kda_verify(*tok_dev(tok), slots)
+    Oo = o.verify(tok.np, slots)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
+    check_out(O, Oo, v=tok.np["v"])
+    na = np.array([P - 1, P // 2], dtype=np.int32)
+    g.kda_commit(slots, torch.from_numpy(na).to("cuda"))
+    o.commit(slots, na)
+    torch.cuda.synchronize()
+    check_state(g.state[slots.tolist()], o.state[slots])
+    meta_equal(g.meta_array(), o.meta(), slots)
     assert device_errors(g) == 0
 
 
