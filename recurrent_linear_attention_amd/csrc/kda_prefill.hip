@@ -601,6 +601,20 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_wave_ba
       : "v"(gsrc), "s"(lds_wave_base)
       : "memory");
 }
+// 4 bytes per lane (global_load_lds_dword): lane i writes lds_wave_base + 4 i. Used only to
+// bring lines into L2 ahead of their LDS-direct loads; the LDS bytes it writes are never read.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_wave_base)
+      : "memory");
+}
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -709,9 +723,25 @@ struct StateFetch {
 // the counts leave that load out, so that wave waits for slightly more than it needs.
 // A state-pass work-group has SCW compute waves (one per 16-column tile of a 128-column slice)
 // and SLW load waves; a work-group on a narrower slice ends its surplus compute waves at once
-// (a barrier counts only the waves still running).
+// (a barrier counts only the waves still running), except wave SCW - 1, the prefetch wave.
 constexpr int SCW = PD / 16;
 constexpr int SLW = 4;
+
+// L2 prefetch. The LDS-direct loads of a chunk wait on HBM (the operand blocks and the V rows
+// are not in L2 when their group is issued, ~1.7 chunks ahead of use), and the chain's pace is
+// set by that latency. Below 128 columns the last compute-wave position (wave SCW - 1) has no
+// state tile and becomes a prefetch wave: after the first barrier of chunk c it touches every
+// 128-byte line of chunk c + PF's operand block and of its 64 V rows (all columns of the head),
+// split over the head's slices, with 4-byte LDS-direct loads into a 256-byte LDS area nobody
+// reads. It never waits for them (its vmcnt is its own), so the load waves then find the lines
+// in L2: one 8192-token prompt at 16-column slices, state pass 200 -> 183 us. The prefetched
+// chunks of the four heads an XCD holds at 16 columns take ~1.5 MiB of its 4 MiB L2; at 32
+// columns and wider (more heads per XCD) the prefetch measured no gain and is left off.
+constexpr int PF_LINES = BLOCK_BYTES / 128 + 2 * PC;        // 484 block lines + 128 V lines
+constexpr int PF_INSTR = (PF_LINES + 63) / 64;               // 10 wave instructions per chunk
+static_assert(BLOCK_BYTES % 128 == 0, "whole lines");
+constexpr int PF_LDS = 256;                                  // the prefetch wave's LDS area
+__host__ __device__ constexpr int prefetch_distance(int vsw) { return vsw == 16 ? 4 : 0; }
 
 // The pass of (sequence, head) chain hg (rank hg / H by length, head hg % H) over value
 // columns [VSW vs, VSW (vs + 1)), on the work-group's LDS (two chunk images of StateBuf<VSW>).
@@ -721,7 +751,7 @@ __device__ __forceinline__ void state_pass_body(const PoolView& P, const Prefill
                                                 const int32_t* __restrict__ ckoff,
                                                 const int32_t* __restrict__ order,
                                                 const char* __restrict__ blocks, int hg, int vs,
-                                                int wave, char* lds_base) {
+                                                int wave, char* lds_base, uint32_t pf_lds) {
   constexpr int TPW = 1;                    // 16-column tiles per compute wave
   constexpr int LW = SLW;
   constexpr int NTL = 64 * LW;              // load-issuing threads
@@ -733,7 +763,8 @@ __device__ __forceinline__ void state_pass_body(const PoolView& P, const Prefill
   constexpr int WAIT_BS = SF::N_KV + SF::N_QTA + N_KBG + SF::N_KV;
   static_assert(WAIT_BX <= 63 && WAIT_BW <= 63 && WAIT_BS <= 63, "vmcnt holds at most 63");
   const int H = P.H, h = hg % H, si = order[hg / H];
-  // Load waves are waves SCW .. SCW + LW - 1; t and w index within a role.
+  // Load waves are waves SCW .. SCW + LW - 1; t and w index within a role. Below 128 columns
+  // wave SCW - 1 prefetches (it is past the compute waves).
   const bool loads = wave >= SCW;
   const int w = loads ? wave - SCW : wave, t = (int)threadIdx.x - 64 * (wave - w),
             l = t & 63, l16 = l & 15, lq = l >> 4;
@@ -755,6 +786,41 @@ __device__ __forceinline__ void state_pass_body(const PoolView& P, const Prefill
   auto sf = [&](int c) __attribute__((always_inline)) {   // past the last chunk: repeat it
     return SF(blk0, A, min(c, nlast), H, lo, len, h, col0, t, (c & 1) ? lds1 : lds0);
   };
+  if (!loads && wave >= VSW / 16) {
+    // ---- prefetch wave (VSW < 128) --------------------------------------------------------------
+    constexpr int PF = prefetch_distance(VSW), NVS = PD / VSW;
+    if constexpr (PF > 0) {
+      auto prefetch = [&](int cc) __attribute__((always_inline)) {
+        if (cc > nlast) return;
+        int t0, n;
+        chunk_span(cc, len, PC, A.ckpt_interval, &t0, &n);
+        const char* b = blk0 + (size_t)cc * H * BLOCK_BYTES;
+        const char* vrow =
+            reinterpret_cast<const char*>(A.t.v + (size_t)(lo + t0) * H * PD + (size_t)h * PD);
+        for (int j = vs; j < PF_INSTR; j += NVS) {
+          const int x = 64 * j + l;   // line x: block lines, then V rows (two lines each)
+          const char* a;
+          if (x < BLOCK_BYTES / 128) {
+            a = b + 128 * x;
+          } else {
+            const int y = min(x - BLOCK_BYTES / 128, 2 * PC - 1);
+            a = vrow + (size_t)min(y >> 1, n - 1) * hst2 + 128 * (y & 1);
+          }
+          lds_dma4(a, pf_lds);
+        }
+      };
+      for (int c = 2; c < PF; ++c) prefetch(c);
+      for (int c = 0; c < nch; ++c) {
+        lds_barrier();   // BX
+        prefetch(c + PF);
+        lds_barrier();   // BW
+        lds_barrier();   // BS
+      }
+      vm_wait<0>();
+      if (A.out_slot[si] >= 0 && A.out_slot[si] < P.num_slots) __syncthreads();
+    }
+    return;
+  }
   if (loads) {
     // ---- load waves ------------------------------------------------------------------------
     if (nch > 0) {
@@ -995,6 +1061,7 @@ __global__ __launch_bounds__(64 * (SCW + SLW)) void state_pass_kernel(PoolView P
                                                                      const int32_t* __restrict__ order,
                                                                      const char* __restrict__ blocks) {
   __shared__ __attribute__((aligned(16))) char lds[2 * StateBuf<PD, 64 * SLW>::BYTES];
+  extern __shared__ __attribute__((aligned(16))) char state_pass_dyn[];   // PF_LDS bytes used
   const StatePlan& sp = A.plan;
   const int bid = blockIdx.x;
   int g = 0;
@@ -1005,13 +1072,14 @@ __global__ __launch_bounds__(64 * (SCW + SLW)) void state_pass_kernel(PoolView P
   if (hgl >= (sp.rank_end[g] - r0) * P.H) return;
   // the wave index is uniform: derived addresses (buffer descriptors among them) stay scalar
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  if (wave < SCW && wave >= vsw / 16) return;
+  if (wave < SCW && wave >= vsw / 16 && !(wave == SCW - 1 && prefetch_distance(vsw) > 0)) return;
   const int hg = r0 * P.H + hgl, vs = m % nvs;
+  const uint32_t pf = (uint32_t)(uintptr_t)state_pass_dyn;
   switch (vsw) {
-    case 16: state_pass_body<16>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
-    case 32: state_pass_body<32>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
-    case 64: state_pass_body<64>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
-    default: state_pass_body<128>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds); break;
+    case 16: state_pass_body<16>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds, pf); break;
+    case 32: state_pass_body<32>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds, pf); break;
+    case 64: state_pass_body<64>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds, pf); break;
+    default: state_pass_body<128>(P, A, choff, ckoff, order, blocks, hg, vs, wave, lds, pf); break;
   }
 }
 
@@ -1236,7 +1304,7 @@ hipError_t launch_state(const PoolView& p, const PrefillLaunch& a, const int32_t
   // with a state-pass work-group: in a mixed batch the decode and verify kernels on the side
   // stream then run on the CUs the pass leaves free instead of slowing its sequential chain.
   constexpr int lds_static = 2 * StateBuf<PD, 64 * SLW>::BYTES;
-  static_assert(lds_static <= LDS_PER_CU, "state pass LDS image");
+  static_assert(lds_static + PF_LDS <= LDS_PER_CU, "state pass LDS image and prefetch area");
   hipLaunchKernelGGL(state_pass_kernel, dim3(nb), dim3(64 * (SCW + SLW)), LDS_PER_CU - lds_static, s, p,
                      a, choff, ckoff, order, blocks);
   return hipGetLastError();
