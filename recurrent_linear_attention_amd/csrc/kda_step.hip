@@ -16,9 +16,11 @@
 // RPT consecutive key rows x 4 consecutive columns (one float4 per row). The reductions over
 // key rows (u, p and k.q) go first through the thread's own rows, then a butterfly across
 // the lanes of a wave that hold the same columns (DPP and lane-swap instructions), then
-// across waves through LDS in wave order. Decode, verify and commit use the same layout and
-// the same step function, so a commit that replays n positions yields the state bit-for-bit
-// equal to n decode calls.
+// across waves through LDS in wave order. Decode and commit (and verify of more than 16
+// positions, and the direct per-draft scheme) use the same layout and the same step function,
+// so a commit that replays n positions yields the state bit-for-bit equal to n decode calls.
+// Verify of up to 16 positions at d = 128 writes no state and solves its positions together in
+// WY form instead (verify_wy_kernel).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -325,18 +327,38 @@ __device__ __forceinline__ void ring_append(const PoolView& P, const StepTensors
                                             int slot, int head) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   constexpr int CPP = D / 2;                       // 16-byte pieces per position: k D/8, v D/8, a D/4
-  const int t = threadIdx.x, R = P.R, total = n_pos * CPP;
-  for (int x = t; x < total; x += blockDim.x) {
+  constexpr int NB = 4;                            // pieces per thread in flight together
+  const int t = threadIdx.x, R = P.R, total = n_pos * CPP, nt = blockDim.x;
+  auto src_of = [&](int x) -> const u4* {
     const int j = x / CPP, u = x % CPP;
-    const size_t src = ((size_t)bi * n_pos + j) * P.H + h, dst = ((size_t)slot * R + ring_at(head, j, R)) * P.H + h;
-    if (u < D / 8)
-      reinterpret_cast<u4*>(P.ring_k + dst * D)[u] = reinterpret_cast<const u4*>(T.k + src * D)[u];
-    else if (u < D / 4)
-      reinterpret_cast<u4*>(P.ring_v + dst * D)[u - D / 8] = reinterpret_cast<const u4*>(T.v + src * D)[u - D / 8];
-    else
-      reinterpret_cast<u4*>(P.ring_a + dst * D)[u - D / 4] = reinterpret_cast<const u4*>(T.a + src * D)[u - D / 4];
+    const size_t src = ((size_t)bi * n_pos + j) * P.H + h;
+    if (u < D / 8) return reinterpret_cast<const u4*>(T.k + src * D) + u;
+    if (u < D / 4) return reinterpret_cast<const u4*>(T.v + src * D) + (u - D / 8);
+    return reinterpret_cast<const u4*>(T.a + src * D) + (u - D / 4);
+  };
+  auto dst_of = [&](int x) -> u4* {
+    const int j = x / CPP, u = x % CPP;
+    const size_t dst = ((size_t)slot * R + ring_at(head, j, R)) * P.H + h;
+    if (u < D / 8) return reinterpret_cast<u4*>(P.ring_k + dst * D) + u;
+    if (u < D / 4) return reinterpret_cast<u4*>(P.ring_v + dst * D) + (u - D / 8);
+    return reinterpret_cast<u4*>(P.ring_a + dst * D) + (u - D / 4);
+  };
+  // NB loads issued before their stores: the inputs and the ring never overlap, and the stores
+  // would otherwise hold each next load back (one memory round trip per piece)
+  for (int x0 = t; x0 < total; x0 += NB * nt) {
+    u4 buf[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int x = x0 + i * nt;
+      buf[i] = *src_of(x < total ? x : x0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int x = x0 + i * nt;
+      if (x < total) *dst_of(x) = buf[i];
+    }
   }
-  for (int j = t; j < n_pos; j += blockDim.x)
+  for (int j = t; j < n_pos; j += nt)
     P.ring_b[((size_t)slot * R + ring_at(head, j, R)) * P.H + h] = T.b[((size_t)bi * n_pos + j) * P.H + h];
 }
 
@@ -386,6 +408,308 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
   });
   if (t == 0 && h == 0 && vs == 0) {
     P.meta[slot].v_base = head;
+    P.meta[slot].v_npos = n_pos;
+    P.meta[slot].pending = n_pos;
+  }
+}
+
+// ---- verify of up to 16 positions in WY form (d = 128) -------------------------------------
+// Unrolling the step over the verify's positions j = 0 .. P-1 from the committed state S (G_j =
+// a_0 ... a_j per key channel, delta_j the step's b_j (v_j - u_j)):
+//   S_j = Diag(G_j) S + sum_{m<=j} Diag(G_j / G_m) k_m delta_m^T, so
+//   delta_j = b_j (v_j - S^T (G_j k_j) - sum_{m<j} A[j][m] delta_m),  A[j][m]  = sum_i k_j k_m G_j / G_m
+//   o_j     = S^T (G_j q_j) + sum_{m<=j} Aq[j][m] delta_m,              Aq[j][m] = sum_i q_j k_m G_j / G_m
+// (G_j / G_m = a_{m+1} ... a_j): Delta = T (V - (G K) S) with T = (I + Diag(b) A)^-1 Diag(b) and
+// O = (G Q) S + Aq Delta. No position waits for the one before it: the products run on fp32
+// matrix cores (v_mfma_f32_16x16x4_f32), and only the 16 x 16 inverse is sequential. A key
+// channel whose decay over the P positions is below 2^-60 (k_m / G_m could leave the fp32 range)
+// takes no part in the factored A products; its terms are added exactly from the raw inputs.
+// Work-group: (sequence, head, 64 value columns), four waves of one 16-column tile each; waves
+// 0-1 also compute the key channels' decays and the two key-channel halves of A, waves 2-3 stage
+// V and compute the halves of Aq, and wave 0 the inverse. As in verify_kernel the launch ends
+// with B * H ring-append work-groups, and no state is written.
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int VCP = 16;                 // positions of the WY verify (at most)
+constexpr int VC_COLS = 64;             // value columns per work-group
+constexpr int VC_NCS = 128 / VC_COLS;   // work-groups per (sequence, head)
+constexpr int VC_NT = 256;
+constexpr float VC_DECAY_MIN = 0x1p-60f;
+static_assert(VCP * 128 / 2 <= 4 * VC_NT, "one ring-append batch per thread");
+
+struct VerifyLds {
+  float gk[VCP][132];          // G_j k_j  (rows j >= P zero)
+  float gq[VCP][132];          // G_j q_j
+  float ki[VCP][132];          // k_m / G_m, zero on fast channels
+  float at[2][VCP][VCP];       // A halves (waves 0, 1), row-major
+  float aq[2][VCP][VCP + 1];   // Aq halves (waves 2, 3)
+  float tm[VCP][VCP + 1];      // T
+  float v[VCP][VC_COLS];       // V of the work-group's columns
+  float b[VCP];
+  uint64_t fast[2];            // key channels decaying below VC_DECAY_MIN
+};
+
+// the value of lane `src` of each group of four lanes, to all four (DPP quad_perm)
+__device__ __forceinline__ float quad_bcast(float x, int src) {
+  const int v = __float_as_int(x);
+  switch (src) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
+  }
+}
+
+__device__ __forceinline__ f4v mfma4(float a, float b, f4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Ring append of the WY verify (n_pos <= 16): every input piece is loaded before the slot and
+// its ring head are awaited, then stored (one memory round trip for the copy).
+__device__ __forceinline__ void ring_append_wy(const PoolView& P, const StepTensors& T, int np, int bi, int h,
+                                               const int32_t* __restrict__ slots) {
+  constexpr int D = 128, CPP = D / 2;   // 16-byte pieces per position: k D/8, v D/8, a D/4
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const int t = threadIdx.x, total = np * CPP;
+  auto piece = [&](int x, int& u) -> size_t {   // row of piece x, u its index in the row
+    u = x % CPP;
+    return (size_t)(x / CPP);
+  };
+  u4 buf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int u;
+    const size_t j = piece(min(t + VC_NT * i, total - 1), u);
+    const size_t src = ((size_t)bi * np + j) * P.H + h;
+    buf[i] = u < D / 8   ? reinterpret_cast<const u4*>(T.k + src * D)[u]
+             : u < D / 4 ? reinterpret_cast<const u4*>(T.v + src * D)[u - D / 8]
+                         : reinterpret_cast<const u4*>(T.a + src * D)[u - D / 4];
+  }
+  const float bb = T.b[((size_t)bi * np + min(t, np - 1)) * P.H + h];
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) return;   // flagged by the WY work-groups
+  const int R = P.R, head = wrap(P.meta[slot].ring_head, R);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int x = t + VC_NT * i;
+    if (x < total) {
+      int u;
+      const size_t j = piece(x, u);
+      const size_t dst = ((size_t)slot * R + ring_at(head, (int)j, R)) * P.H + h;
+      if (u < D / 8)
+        reinterpret_cast<u4*>(P.ring_k + dst * D)[u] = buf[i];
+      else if (u < D / 4)
+        reinterpret_cast<u4*>(P.ring_v + dst * D)[u - D / 8] = buf[i];
+      else
+        reinterpret_cast<u4*>(P.ring_a + dst * D)[u - D / 4] = buf[i];
+    }
+  }
+  if (t < np) P.ring_b[((size_t)slot * R + ring_at(head, t, R)) * P.H + h] = bb;
+}
+
+__global__ __launch_bounds__(VC_NT) void verify_wy_kernel(PoolView P, StepTensors T, int n_pos,
+                                                          const int32_t* __restrict__ slots) {
+  constexpr int D = 128;
+  __shared__ VerifyLds L;
+  // the wave index is uniform: the role branches below are scalar
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, i16 = l & 15, g = l >> 4;
+  const int np = n_pos;
+  const size_t HD = (size_t)P.H * D;
+  const int n_wy = gridDim.x / (VC_NCS + 1) * VC_NCS;   // WY work-groups; the rest append
+  if ((int)blockIdx.x >= n_wy) {
+    const int hb = blockIdx.x - n_wy;
+    ring_append_wy(P, T, np, hb / P.H, hb % P.H, slots);
+    return;
+  }
+  const int cs = blockIdx.x % VC_NCS, h = (blockIdx.x / VC_NCS) % P.H, bi = blockIdx.x / (VC_NCS * P.H);
+  const int ct = 16 * w, c0 = cs * VC_COLS + ct;   // the wave's tile (in the slice, in the head)
+  // Every input load is issued before any is used, and before the slot index (which the state
+  // tile's address needs) is awaited: waves 0-1 the positions' k, q and a of key channel i = t
+  // (rows past P re-read row P - 1 and are masked), waves 2-3 the V columns and b. The bf16
+  // words are converted only once all loads are issued, so no load waits on an earlier one.
+  constexpr int NV = VCP * VC_COLS / 128;   // V values per thread of waves 2-3
+  uint32_t kw[VCP], qw[VCP], vw[NV];
+  float ar[VCP], bv = 0.f;
+  if (w < 2) {
+#pragma unroll
+    for (int j = 0; j < VCP; ++j) {
+      const size_t row = ((size_t)bi * np + min(j, np - 1)) * HD + (size_t)h * D + t;
+      kw[j] = T.k[row];
+      qw[j] = T.q[row];
+      ar[j] = T.a[row];
+    }
+  } else {
+    const int u = t - D;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int e = u + 128 * x, j = e / VC_COLS, c = e % VC_COLS;
+      vw[x] = T.v[((size_t)bi * np + min(j, np - 1)) * HD + (size_t)h * D + cs * VC_COLS + c];
+    }
+    bv = T.b[((size_t)bi * np + min(u % VCP, np - 1)) * P.H + h];
+  }
+  const int slot = slots[bi];
+  if (slot < 0 || slot >= P.num_slots) {
+    if (t == 0 && h == 0 && cs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
+    return;
+  }
+  // the wave's state tile as the B operand of the K = 128 products (K index 32 g + s):
+  // sv[s] = S[32 g + s][c0 + i16]
+  float sv[32];
+  {
+    const float* Sp = P.state + ((size_t)slot * P.H + h) * D * D + c0 + i16;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) sv[s] = Sp[(size_t)(32 * g + s) * D];
+  }
+  // keeps the compiler from merging the role branches (which would place the slot read and the
+  // state loads after the first use of the inputs: two memory round trips instead of one)
+  asm volatile("" ::: "memory");
+  if (w < 2) {
+    // key channel i = t: running decay over the positions, the decayed rows and k / G
+    const int i = t;
+    float G = 1.f, gmin = 1.f;
+#pragma unroll
+    for (int j = 0; j < VCP; ++j) {
+      const bool live = j < np;
+      const float kr = live ? bf2f(kw[j]) : 0.f, qr = live ? bf2f(qw[j]) : 0.f;
+      G = live ? G * ar[j] : G;
+      gmin = fminf(gmin, G);
+      L.gk[j][i] = G * kr;
+      L.gq[j][i] = G * qr;
+      ar[j] = kr * __builtin_amdgcn_rcpf(G);   // k / G, stored below unless the channel is fast
+    }
+    const bool fast = !(gmin >= VC_DECAY_MIN);   // NaN decays take the exact path too
+#pragma unroll
+    for (int j = 0; j < VCP; ++j) L.ki[j][i] = fast ? 0.f : ar[j];
+    const uint64_t m = __ballot(fast);
+    if (l == 0) L.fast[w] = m;
+  } else {
+    const int u = t - D;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int e = u + 128 * x, j = e / VC_COLS, c = e % VC_COLS;
+      L.v[j][c] = j < np ? bf2f(vw[x]) : 0.f;
+    }
+    if (u < VCP) L.b[u] = u < np ? bv : 0.f;
+  }
+  __syncthreads();
+
+  // products with K = 128 on the wave's tile, K index 32 g + s
+  auto tile_product = [&](const float(*X)[132]) __attribute__((always_inline)) {
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const f4v xa = *reinterpret_cast<const f4v*>(&X[i16][32 * g + 4 * s4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma4(xa[e], sv[4 * s4 + e], acc);
+    }
+    return acc;
+  };
+  {
+    // A (waves 0-1) and Aq (waves 2-3) over key channels [64 (w & 1), 64 (w & 1) + 64): the
+    // 16 x 16 results of [16 x 64] x [64 x 16], K index 64 (w & 1) + 16 g + s
+    const float(*X)[132] = w < 2 ? L.gk : L.gq;
+    const int kb = 64 * (w & 1) + 16 * g;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const f4v xa = *reinterpret_cast<const f4v*>(&X[i16][kb + 4 * s4]);
+      const f4v ka = *reinterpret_cast<const f4v*>(&L.ki[i16][kb + 4 * s4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma4(xa[e], ka[e], acc);
+    }
+    if ((w & 1) == 0 && (L.fast[0] | L.fast[1])) {
+      // exact terms of the fast channels: element (j, m) = (4 g + e, i16)
+      for (int wd = 0; wd < 2; ++wd) {
+        uint64_t fm = L.fast[wd];
+        while (fm) {
+          const int i = 64 * wd + __builtin_ctzll(fm);
+          fm &= fm - 1;
+          const int m = i16;
+          const float km = m < np ? bf2f(T.k[((size_t)bi * np + m) * HD + (size_t)h * D + i]) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * g + e;
+            if (j < np && m < np && (w == 0 ? j > m : j >= m)) {
+              float prod = 1.f;
+              for (int tt = m + 1; tt <= j; ++tt) prod *= T.a[((size_t)bi * np + tt) * HD + (size_t)h * D + i];
+              const size_t rj = ((size_t)bi * np + j) * HD + (size_t)h * D + i;
+              const float xj = w == 0 ? bf2f(T.k[rj]) : bf2f(T.q[rj]);
+              acc[e] = __builtin_fmaf(xj * km, prod, acc[e]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (w < 2)
+        L.at[w][4 * g + e][i16] = acc[e];
+      else
+        L.aq[w - 2][4 * g + e][i16] = acc[e];
+    }
+  }
+  // P = (G K) S and R = (G Q) S on the wave's tile
+  const f4v pa = tile_product(L.gk), ra = tile_product(L.gq);
+  __syncthreads();
+  if (w == 0) {
+    // T = (I + Diag(b) A)^-1 Diag(b) by forward substitution, column m = l / 4 on the four lanes
+    // of a quad: lane q keeps the running sums of rows j = 4 k + q. Step r: x_r = [r = m] -
+    // acc_r on the lane that holds row r, broadcast to its quad (DPP), then every row j > r
+    // takes b_j A[j][r] x_r. The coefficients (zero unless j > r; A is zero on rows and columns
+    // past P) are read once, up front.
+    const int m = l >> 2, q = l & 3;
+    f4v lr[4][4];   // lr[k][c][e] = b_j A[j][4 c + e] for j = 4 k + q > 4 c + e, else 0
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = 4 * k + q;
+      const float bj = L.b[j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f4v a = *reinterpret_cast<const f4v*>(&L.at[0][j][4 * c]) + *reinterpret_cast<const f4v*>(&L.at[1][j][4 * c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lr[k][c][e] = j > 4 * c + e ? bj * a[e] : 0.f;
+      }
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f}, xv[VCP];
+#pragma unroll
+    for (int r = 0; r < VCP; ++r) {
+      const float own = (r == m ? 1.f : 0.f) - acc[r >> 2];   // x_r on lane q = r % 4
+      xv[r] = quad_bcast(own, r & 3);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(lr[k][r >> 2][r & 3], xv[r], acc[k]);
+    }
+    // lane q stores rows 4 k + q (no store inside the chain: it would wait on the reads above)
+    const float bm = L.b[m];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x = q == 0 ? xv[4 * k] : q == 1 ? xv[4 * k + 1] : q == 2 ? xv[4 * k + 2] : xv[4 * k + 3];
+      L.tm[4 * k + q][m] = x * bm;
+    }
+  }
+  __syncthreads();
+  {
+    // Delta = T (V - P), O = R + Aq Delta on the wave's tile: K = 16 with index 4 g + s, so the
+    // accumulator tiles (rows 4 g + e) are the B operands as they stand
+    f4v xv, dv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xv[e] = L.v[4 * g + e][ct + i16] - pa[e];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dv = mfma4(L.tm[i16][4 * g + s], xv[s], dv);
+    f4v ov = ra;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int m = 4 * g + s;
+      const float aq = i16 >= m ? L.aq[0][i16][m] + L.aq[1][i16][m] : 0.f;
+      ov = mfma4(aq, dv[s], ov);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      if (j < np)
+        T.o[((size_t)bi * np + j) * HD + (size_t)h * D + c0 + i16] = (uint16_t)(pack_bf2(ov[e], 0.f) & 0xffffu);
+    }
+  }
+  if (t == 0 && h == 0 && cs == 0) {
+    P.meta[slot].v_base = wrap(P.meta[slot].ring_head, P.R);
     P.meta[slot].v_npos = n_pos;
     P.meta[slot].pending = n_pos;
   }
@@ -560,7 +884,9 @@ hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, con
 
 hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
                          const int32_t* d_slots, hipStream_t s) {
-  if (p.dk == 128)
+  if (p.dk == 128 && n_pos <= VCP)
+    hipLaunchKernelGGL(verify_wy_kernel, dim3(B * p.H * (VC_NCS + 1)), dim3(VC_NT), 0, s, p, t, n_pos, d_slots);
+  else if (p.dk == 128)
     hipLaunchKernelGGL(verify_kernel<128>, dim3(step_blocks<128>(p, B) + B * p.H), dim3(StepCfg<128>::NT), 0, s, p,
                        t, n_pos, d_slots);
   else

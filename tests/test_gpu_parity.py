@@ -427,8 +427,10 @@ def test_direct_per_draft_checkpoints_match_ring_scheme(d):
     Or = r.kda_verify(*tok_dev(tok), slots)
     Oo, states_o = o.verify_direct(tok.np, slots)
     torch.cuda.synchronize()
-    assert torch.equal(O, Or), "direct verify outputs must equal the ring verify's"
+    # the direct scheme steps position by position (it stores every draft state); the ring verify
+    # of up to 16 positions solves them at once in WY form: both against the oracle
     check_out(O, Oo, v=tok.np["v"])
+    check_out(Or, Oo, v=tok.np["v"])
     check_state(draft, states_o)
     assert torch.equal(g.state, before), "direct verify must not write any committed state"
     meta_equal(g.meta_array(), o.meta(), slots)
