@@ -426,8 +426,9 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void verify_kernel(PoolView P, Step
 // takes no part in the factored A products; its terms are added exactly from the raw inputs.
 // Work-group: (sequence, head, 64 value columns), four waves of one 16-column tile each; waves
 // 0-1 also compute the key channels' decays and the two key-channel halves of A, waves 2-3 stage
-// V and compute the halves of Aq, and wave 0 the inverse. As in verify_kernel the launch ends
-// with B * H ring-append work-groups, and no state is written.
+// V and compute the halves of Aq, and wave 0 the inverse (while the others compute their tiles'
+// P and R). As in verify_kernel the launch ends with B * H ring-append work-groups, and no state
+// is written.
 typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int VCP = 16;                 // positions of the WY verify (at most)
 constexpr int VC_COLS = 64;             // value columns per work-group
@@ -647,8 +648,6 @@ __global__ __launch_bounds__(VC_NT) void verify_wy_kernel(PoolView P, StepTensor
         L.aq[w - 2][4 * g + e][i16] = acc[e];
     }
   }
-  // P = (G K) S and R = (G Q) S on the wave's tile
-  const f4v pa = tile_product(L.gk), ra = tile_product(L.gq);
   __syncthreads();
   if (w == 0) {
     // T = (I + Diag(b) A)^-1 Diag(b) by forward substitution, column m = l / 4 on the four lanes
@@ -685,6 +684,9 @@ __global__ __launch_bounds__(VC_NT) void verify_wy_kernel(PoolView P, StepTensor
       L.tm[4 * k + q][m] = x * bm;
     }
   }
+  // P = (G K) S and R = (G Q) S on the wave's tile (wave 0 after the inverse, the others
+  // meanwhile)
+  const f4v pa = tile_product(L.gk), ra = tile_product(L.gq);
   __syncthreads();
   {
     // Delta = T (V - P), O = R + Aq Delta on the wave's tile: K = 16 with index 4 g + s, so the
