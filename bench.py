@@ -66,9 +66,9 @@ PREFILL_FLOP_TOK_HEAD = 6 * D * D + C * (3 * D + 2 * D) + C * C / 3
 # (FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them: factors 2.0 and 1.0). Valid
 # only for the kernel source it was measured on (first 16 hex digits of its SHA-256); for any
 # other source the bench reports traffic as null.
-PREFILL_TRAFFIC = {"source_sha256_16": "14a7918b594d58ac", "fetch_scale": 2.0, "write_scale": 1.0,
-                   "fetch_kib": {"chunk_prep_kernel": 269337, "state_pass_kernel": 316228},
-                   "write_kib": {"chunk_prep_kernel": 501494, "state_pass_kernel": 142817}}
+PREFILL_TRAFFIC = {"source_sha256_16": "eafba37a442e28de", "fetch_scale": 2.0, "write_scale": 1.0,
+                   "fetch_kib": {"chunk_prep_kernel": 269337, "state_pass_kernel": 316235},
+                   "write_kib": {"chunk_prep_kernel": 501497, "state_pass_kernel": 142818}}
 
 
 def prefill_traffic_bytes():
