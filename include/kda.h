@@ -186,12 +186,15 @@ typedef struct {
 } kda_step_args;
 
 /* One token per sequence against its slot: the state is read once, updated and written
- * back in place; pos += 1. ("Kimi K3 is here: efficient day-0 support on vLLM", summary:
- * fused kernels for KDA decode.)                                                           */
+ * back in place; pos += 1. A batch of at most 64 sequences takes its slot indices from
+ * h_slots (passed to the kernel by value, so d_slots is not read); larger batches read
+ * d_slots. ("Kimi K3 is here: efficient day-0 support on vLLM", summary: fused kernels for
+ * KDA decode.)                                                                             */
 kda_status kda_decode(kda_pool* pool, const kda_step_args* args, void* stream);
 
-/* Speculative verify of n_pos = 1 + T positions (1 <= n_pos <= ring_cap): steps a register
- * copy of the committed state through the positions, writes o for each, and appends each
+/* Speculative verify of n_pos = 1 + T positions (1 <= n_pos <= ring_cap): computes o for
+ * every position from the committed state (at dk = 128 and n_pos <= 16 all positions at once
+ * in WY form, otherwise by stepping a register copy of the state), and appends each
  * position's (k, v, a, b) to the slot's ring from ring_head on (mod ring_cap). The committed
  * state is NOT written. Marks the slot pending (v_base = ring_head, v_npos = pending = n_pos).
  * ("vLLM lifts Kimi K3 throughput by up to 2.8x", section "ReplaySSM shrinks rollback state":

@@ -57,7 +57,10 @@ struct PrefillLaunch {
   StatePlan plan;              // from plan_state_pass (host lengths)
 };
 
-hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B,
+// Decode takes the host copy of the slot indices too: a batch of at most SLOT_ARG_MAX
+// sequences passes them by value among the kernel arguments.
+constexpr int SLOT_ARG_MAX = 64;
+hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, const int32_t* h_slots,
                          const int32_t* d_slots, hipStream_t s);
 hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
                          const int32_t* d_slots, hipStream_t s);

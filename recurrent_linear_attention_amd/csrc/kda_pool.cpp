@@ -403,7 +403,7 @@ kda_status kda_decode(kda_pool* p, const kda_step_args* a, void* stream) {
   if (st != KDA_OK) return st;
   if (!a->d_slots) return fail(KDA_EINVAL, "null device slot array");
   hipError_t e = kda::launch_decode(p->view, tensors(a->q, a->k, a->v, a->a, a->b, a->o), a->B,
-                                    a->d_slots, as_stream(stream));
+                                    a->h_slots, a->d_slots, as_stream(stream));
   return e == hipSuccess ? KDA_OK : hip_fail(e, "decode launch");
 }
 
@@ -531,7 +531,7 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
         if (e != hipSuccess) return e;
       }
       if (m->n_decode > 0) {
-        e = kda::launch_decode(p->view, dec, m->n_decode, m->d_decode_slots, on);
+        e = kda::launch_decode(p->view, dec, m->n_decode, m->h_decode_slots, m->d_decode_slots, on);
         if (e != hipSuccess) return e;
       }
       if (m->n_verify > 0)

@@ -286,15 +286,24 @@ __device__ __forceinline__ void stepped_positions(int n, float (&S)[C::RPT][4], 
   }
 }
 
-// grid: B * H * (D / VS); block (bi, h, vs) with vs fastest.
-template <int D>
-__global__ __launch_bounds__(StepCfg<D>::NT) void decode_kernel(PoolView P, StepTensors T,
+// Slot indices of a decode batch of at most SLOT_ARG_MAX sequences, by value among the kernel
+// arguments (decode_kernel<D, true>; larger batches read the device array). The kernel's
+// arguments are loaded before anything else, so the state tile's address then waits for no
+// load of its own (16 sequences, cold, by events: 21.8 -> 21.2 us).
+struct SlotArg {
+  int32_t id[SLOT_ARG_MAX];
+};
+
+// grid: (H * (D / VS), B); block (vs, h) with vs fastest in x, the sequence bi in y (no kernel
+// argument is needed to find bi, so its slot index loads with the arguments).
+template <int D, bool BY_VALUE>
+__global__ __launch_bounds__(StepCfg<D>::NT) void decode_kernel(PoolView P, StepTensors T, SlotArg sa,
                                                                 const int32_t* __restrict__ slots) {
   using C = StepCfg<D>;
   __shared__ StepLds<C> lds;
   constexpr int NVS = D / C::VS;
-  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
-  const int slot = slots[bi];
+  const int vs = blockIdx.x % NVS, h = blockIdx.x / NVS, bi = blockIdx.y;
+  const int slot = BY_VALUE ? sa.id[bi] : slots[bi];
   if (slot < 0 || slot >= P.num_slots) {
     if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
     return;
@@ -875,12 +884,21 @@ int step_blocks(const PoolView& p, int B) { return B * p.H * (D / StepCfg<D>::VS
 
 }  // namespace
 
-hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, const int32_t* d_slots,
-                         hipStream_t s) {
-  if (p.dk == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, t, d_slots);
+hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, const int32_t* h_slots,
+                         const int32_t* d_slots, hipStream_t s) {
+  SlotArg sa{};
+  const bool by_value = B <= SLOT_ARG_MAX;
+  if (by_value)
+    for (int32_t i = 0; i < B; ++i) sa.id[i] = h_slots[i];
+  const dim3 g128(step_blocks<128>(p, 1), B), g16(step_blocks<16>(p, 1), B);
+  if (p.dk == 128 && by_value)
+    hipLaunchKernelGGL((decode_kernel<128, true>), g128, dim3(StepCfg<128>::NT), 0, s, p, t, sa, d_slots);
+  else if (p.dk == 128)
+    hipLaunchKernelGGL((decode_kernel<128, false>), g128, dim3(StepCfg<128>::NT), 0, s, p, t, sa, d_slots);
+  else if (by_value)
+    hipLaunchKernelGGL((decode_kernel<16, true>), g16, dim3(StepCfg<16>::NT), 0, s, p, t, sa, d_slots);
   else
-    hipLaunchKernelGGL(decode_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, t, d_slots);
+    hipLaunchKernelGGL((decode_kernel<16, false>), g16, dim3(StepCfg<16>::NT), 0, s, p, t, sa, d_slots);
   return hipGetLastError();
 }
 
