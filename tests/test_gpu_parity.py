@@ -118,6 +118,29 @@ def test_decode_full_size():
     meta_equal(g.meta_array(), o.meta(), range(w["n_slots"]))
 
 
+@pytest.mark.parametrize("d,B", [(128, 64), (128, 65), (16, 64), (16, 65)])
+def test_decode_slot_ids_by_value_and_from_device(d, B):
+    """Decode takes the slot ids of a batch of at most 64 sequences by value among the kernel
+    arguments and reads the device array for larger batches: both sides of that limit, slots a
+    random permutation of a larger pool, against the oracle, untouched slots unchanged."""
+    H, n_slots = 4, 96
+    rng = np.random.default_rng(640 + B + d)
+    g, o = pools(n_slots, H, d)
+    slots = rng.permutation(n_slots)[:B].astype(np.int32)
+    put_states(g, o, slots, ki.draw_states(rng, B, H, d, d))
+    untouched = sorted(set(range(n_slots)) - set(slots.tolist()))
+    before = g.state[untouched].clone()
+    tok = ki.draw_tokens(rng, (B,), H, d, d)
+    O = g.kda_decode(*tok_dev(tok), slots)
+    Oo = o.decode(tok.np, slots)
+    torch.cuda.synchronize()
+    check_out(O, Oo, v=tok.np["v"])
+    check_state(g.state[slots.tolist()], o.state[slots])
+    assert torch.equal(g.state[untouched], before)
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    assert device_errors(g) == 0
+
+
 # ----------------------------------------------------------------------------- verify / commit
 
 def test_verify_commit_rollback_full_size():
