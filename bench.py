@@ -15,8 +15,9 @@ launches on, in a second pass that issues the step's calls one by one (`kernels`
 
 `configs` times each call on its own workload, cold: before every timed call a 512 MiB write
 evicts the 256 MB Infinity Cache, and a HIP event pair on the call's stream brackets the call
-alone (median and p10 / p90 over the iterations; `ms_warm` = back-to-back calls without the
-eviction, for contrast):
+alone (median and p10 / p90 over the iterations; `ms_clean` = the same with a 512 MiB read as
+the eviction, which leaves clean lines behind: see Cold; `ms_warm` = back-to-back calls without
+an eviction, for contrast):
   * decode_b16: 16 single-token decodes against a 256-slot pool (slots a random permutation);
   * verify_commit_b4: 4 speculative verifies of 1+8 positions, then the ReplaySSM commit of
     the accepted drafts (accepted counts ~ U{0..8});
@@ -201,20 +202,40 @@ def _bw(bytes_, ms):
     return {"alg_bytes": int(bytes_), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def _clean(ms, bytes_):
+    """The clean-eviction timing of a call (see Cold): median and its algorithmic GB/s."""
+    import numpy as np
+    m = float(np.median(np.asarray(ms)))
+    gbs = bytes_ / m / 1e6
+    return {"ms_clean": round(m, 5), "GBps_clean": round(gbs, 1), "hbm_frac_clean": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 class Cold:
-    """Times calls cold: a 512 MiB write (untimed, same stream) evicts the 256 MB Infinity
-    Cache before each timed call; an event pair on the stream brackets the call alone."""
+    """Times calls cold: before each timed call an untimed pass over 512 MiB on the same stream
+    evicts the 256 MB Infinity Cache and the L2s, and an event pair brackets the call alone.
+    Two evictions, which bound the call's HBM cost from both sides:
+      * dirty (`ms`): a 512 MiB write. The caches are then full of dirty lines, so every line
+        the call brings in or writes also writes one of them back: the call pays for its own
+        writes, and for write-backs its reads cause (an over-charge of up to its read bytes);
+      * clean (`ms_clean`): a 512 MiB read of a buffer nothing writes. The caches hold clean
+        lines, so the call's reads cost no write-back, but its own writes may still sit in the
+        caches when it ends (an under-charge of up to its write bytes)."""
 
     def __init__(self, torch, dev):
         self.torch = torch
         self.scratch = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        self.clean_src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        self.scratch.fill_(0.0)   # pushes clean_src's initial writes out of the caches
         self.n = 0
 
-    def evict(self):
+    def evict(self, clean=False):
         self.n += 1
-        self.scratch.fill_(float(self.n))
+        if clean:
+            self.sink = self.clean_src.sum()
+        else:
+            self.scratch.fill_(float(self.n))
 
-    def time(self, iters, calls):
+    def time(self, iters, calls, clean=False):
         """calls: functions run in order each iteration, each timed cold. Returns per-call lists
         of event times (ms)."""
         torch = self.torch
@@ -222,7 +243,7 @@ class Cold:
                for _ in calls] for _ in range(iters)]
         for it in range(iters):
             for j, fn in enumerate(calls):
-                self.evict()
+                self.evict(clean)
                 ev[it][j][0].record()
                 fn()
                 ev[it][j][1].record()
@@ -287,11 +308,12 @@ def bench_decode(torch, kda, ki, dev, cold, iters):
     for _ in range(5):
         call()
     (ms,) = cold.time(iters, [call])
+    (ms_c,) = cold.time(iters, [call], clean=True)
     st = _stats(ms)
     out = {"workload": f"decode: B={B} sequences x 1 token, H={H}, d={D}, pool {w['n_slots']} "
                        "slots (random permutation), fp32 state", **st,
            **_bw(decode_bytes(B, H), st["ms"]), "tokens_per_s": round(B / (st["ms"] / 1e3), 1),
-           "ms_warm": round(cold.warm(iters, call), 5)}
+           **_clean(ms_c, decode_bytes(B, H)), "ms_warm": round(cold.warm(iters, call), 5)}
     del pool
     return out
 
@@ -315,14 +337,17 @@ def bench_verify_commit(torch, kda, ki, dev, cold, iters):
         ver()
         com()
     ms_v, ms_c = cold.time(iters, [ver, com])
+    ms_vc, ms_cc = cold.time(iters, [ver, com], clean=True)
     sv, sc = _stats(ms_v), _stats(ms_c)
     n_rep = int(np.sum(1 + w["n_accepted"]))
     out = {"workload": f"speculative verify of B={B} x 1+{P - 1} positions, then ReplaySSM commit "
                        f"of accepted counts {w['n_accepted'].tolist()} ({n_rep} positions "
                        f"replayed), H={H}, d={D}, pool {w['n_slots']} slots, ring of {w['ring_cap']}",
            "verify": {**sv, **_bw(verify_bytes(B, P, H), sv["ms"]),
-                      "positions_per_s": round(B * P / (sv["ms"] / 1e3), 1)},
-           "commit": {**sc, **_bw(commit_bytes(n_rep, B, H), sc["ms"])},
+                      "positions_per_s": round(B * P / (sv["ms"] / 1e3), 1),
+                      **_clean(ms_vc, verify_bytes(B, P, H))},
+           "commit": {**sc, **_bw(commit_bytes(n_rep, B, H), sc["ms"]),
+                      **_clean(ms_cc, commit_bytes(n_rep, B, H))},
            "committed_tokens_per_s": round(n_rep / ((sv["ms"] + sc["ms"]) / 1e3), 1)}
     del pool
     return out
@@ -344,6 +369,7 @@ def bench_prefill(torch, kda, ki, dev, cold, iters):
     for _ in range(3):
         call()
     (ms,) = cold.time(iters, [call])
+    (ms_c,) = cold.time(iters, [call], clean=True)
     st = _stats(ms)
     byts, fl = prefill_bytes(L, H, n_out=1, n_ckpt=n_ck), prefill_flops(L, H)
     bw = _bw(byts, st["ms"])
@@ -355,7 +381,7 @@ def bench_prefill(torch, kda, ki, dev, cold, iters):
            # the MFMA rate this workload would reach at full HBM bandwidth (arithmetic intensity x
            # 8 TB/s) and the achieved share of it, which equals hbm_frac
            "hbm_bound_TFLOPs": round(fl / byts * HBM_PEAK_GBS / 1e3, 1),
-           "frac_of_hbm_bound_ceiling": bw["hbm_frac"],
+           "frac_of_hbm_bound_ceiling": bw["hbm_frac"], **_clean(ms_c, byts),
            "ms_warm": round(cold.warm(max(iters // 2, 1), call), 5)}
     del pool
     return res
@@ -512,6 +538,7 @@ def main():
         for part in (configs["decode_b16"], configs["verify_commit_b4"]["verify"],
                      configs["verify_commit_b4"]["commit"], configs["prefill_8192"]):
             part["copy_frac"] = round(part["GBps"] / peaks["copy_GBps"], 4)
+            part["copy_frac_clean"] = round(part["GBps_clean"] / peaks["copy_GBps"], 4)
         for part in kernels.values():
             part["copy_frac"] = round(part["GBps"] / peaks["copy_GBps"], 4)
 
