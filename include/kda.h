@@ -220,9 +220,11 @@ kda_status kda_rollback(kda_pool* pool, int32_t B, const int32_t* h_slots,
  * smaller one.) kda_verify_direct is kda_verify except that, instead of appending ring
  * entries, it writes the state after each of its n_pos positions to draft_states
  * ([B][n_pos][H][dk][dv] fp32, device, 16-byte aligned, caller-owned,
- * kda_draft_state_bytes(...) bytes). Outputs o are bit-identical to kda_verify's. The ring is
- * untouched; the slot becomes pending a direct commit (v_base = ring_head, v_npos = pending =
- * n_pos); 1 <= n_pos <= ring_cap as for kda_verify. kda_commit_direct then copies
+ * kda_draft_state_bytes(...) bytes). Outputs o come from the stepping form: bit-identical to
+ * kda_verify's where that steps too (dk = 16, n_pos > 16), equal to its WY form up to
+ * rounding otherwise. The ring is untouched; the slot becomes pending a direct commit
+ * (v_base = ring_head, v_npos = pending = n_pos); 1 <= n_pos <= ring_cap as for kda_verify.
+ * kda_commit_direct then copies
  * draft_states[b][n] (n = d_n_accepted[b], clamped to [0, v_npos - 1] with
  * KDA_DEVERR_NACC_RANGE as in kda_commit) into the slot: the same state kda_commit would
  * build by replay, bit for bit; pos += 1 + n, pending = 0, ring_head unchanged. The commit
