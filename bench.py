@@ -353,6 +353,48 @@ def bench_verify_commit(torch, kda, ki, dev, cold, iters):
     return out
 
 
+def bench_verify_schemes(torch, kda, ki, dev, cold, iters, batches=(4, 16, 64)):
+    """ReplaySSM ring against direct per-draft checkpoints at several verify batch sizes (1+8
+    positions, H = 32): per scheme the cold verify and commit times, the bytes each moves, and
+    the memory each needs beside the committed state (ring entries per slot, draft states per
+    verifying sequence)."""
+    import numpy as np
+    out = {}
+    for B in batches:
+        w = ki.verify_workload(20 + B, B=B, n_slots=max(256, B))
+        H, P = w["H"], w["n_pos"]
+        pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+        for _ in range(w["n_slots"]):
+            pool.kda_slot_alloc()
+        slots = kda.IndexArray(w["slots"], dev)
+        pool.state[w["slots"].tolist()] = w["states"].to(dev)
+        t = w["tokens"]
+        q, k, v, a, b = (x.to(dev).contiguous() for x in (t.q, t.k, t.v, t.a, t.b))
+        o = torch.empty((B, P, H, D), dtype=torch.bfloat16, device=dev)
+        na = torch.from_numpy(w["n_accepted"]).to(dev)
+        draft = pool.kda_draft_states(B, P)
+        calls = [lambda: pool.kda_verify(q, k, v, a, b, slots, o=o),
+                 lambda: pool.kda_commit(slots, na),
+                 lambda: pool.kda_verify_direct(q, k, v, a, b, slots, draft_states=draft, o=o),
+                 lambda: pool.kda_commit_direct(slots, na, draft)]
+        for _ in range(2):
+            for fn in calls:
+                fn()
+        ms = [float(np.median(x)) for x in cold.time(iters, calls)]
+        n_rep = int(np.sum(1 + w["n_accepted"]))
+        ring_b = verify_bytes(B, P, H) + commit_bytes(n_rep, B, H)
+        direct_b = verify_direct_bytes(B, P, H) + commit_direct_bytes(B, H)
+        out[f"B{B}"] = {
+            "ring": {"verify_ms": round(ms[0], 5), "commit_ms": round(ms[1], 5),
+                     "bytes": int(ring_b), "extra_bytes_per_slot": w["ring_cap"] * H * RING_ENTRY_B},
+            "direct": {"verify_ms": round(ms[2], 5), "commit_ms": round(ms[3], 5),
+                       "bytes": int(direct_b), "extra_bytes_per_sequence": P * H * STATE_B},
+            "ring_over_direct_time": round((ms[0] + ms[1]) / (ms[2] + ms[3]), 3)}
+        del pool, draft
+    return {"workload": "verify of B x 1+8 positions and the commit of the accepted drafts, H=32, "
+                        "d=128, ReplaySSM ring against direct per-draft state checkpoints", **out}
+
+
 def bench_prefill(torch, kda, ki, dev, cold, iters):
     w = ki.prefill_workload(3)
     H, L, I = w["H"], w["cu_seqlens"][-1], w["ckpt_interval"]
@@ -531,6 +573,8 @@ def main():
         cold = Cold(torch, dev)
         configs = {"decode_b16": bench_decode(torch, kda, ki, dev, cold, args.config_iters),
                    "verify_commit_b4": bench_verify_commit(torch, kda, ki, dev, cold, args.config_iters),
+                   "verify_schemes": bench_verify_schemes(torch, kda, ki, dev, cold,
+                                                          max(args.config_iters // 5, 3)),
                    "prefill_8192": bench_prefill(torch, kda, ki, dev, cold, max(args.config_iters // 2, 1))}
         del cold
         peaks = measured_peaks(torch, dev)
