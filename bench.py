@@ -395,6 +395,67 @@ def bench_verify_schemes(torch, kda, ki, dev, cold, iters, batches=(4, 16, 64)):
                         "d=128, ReplaySSM ring against direct per-draft state checkpoints", **out}
 
 
+def bench_prefix_hit_and_intervals(torch, kda, ki, dev, cold, iters, aligned_ms):
+    """The two prefix-cache rows beside the 8192-token prefill (H = 32): checkpoints every 1000
+    tokens (not a multiple of the 64-token chunk: every interval gets chunks of its own) against
+    every 1024; and a partial hit, a new 8192-token prompt whose first 6144 tokens match a cached
+    prompt with checkpoints every 1024 tokens, served as the checkpoint copy into the request's
+    slot, the prefill of the remaining 2048 tokens from that slot, then a verify of 1+8 drafts
+    and the commit of the accepted ones on the same slot."""
+    import numpy as np
+    w = ki.prefill_workload(3)
+    H, L = w["H"], w["cu_seqlens"][-1]
+    pool = kda.KDAPool(w["n_slots"], H, D, w["ring_cap"], device=dev)
+    for _ in range(w["n_slots"]):
+        pool.kda_slot_alloc()
+    t = w["tokens"]
+    q, k, v, a, b = (x.to(dev).contiguous() for x in (t.q, t.k, t.v, t.a, t.b))
+    o = torch.empty((L, H, D), dtype=torch.bfloat16, device=dev)
+    cu, out = kda.IndexArray(w["cu_seqlens"], dev), kda.IndexArray([0], dev)
+    # unaligned interval: 8 boundaries at 1000, 2000, ..., 8000
+    I_u = 1000
+    cks_u = kda.IndexArray(list(range(1, 1 + L // I_u)), dev)
+    unal = lambda: pool.kda_prefill(q, k, v, a, b, cu, out, ckpt_slots=cks_u, ckpt_interval=I_u, o=o)  # noqa: E731
+    # partial hit: checkpoint slot 9 holds the cached prompt's state after 6144 tokens (its
+    # sixth 1024-token checkpoint); the request's slot 10 resumes from it
+    hit = kda.prefix_hit(6144, L, 1024)
+    cached, req = 9, 10
+    pool.kda_prefill(q[:hit], k[:hit], v[:hit], a[:hit], b[:hit], kda.IndexArray([0, hit], dev),
+                     kda.IndexArray([cached], dev))
+    rest = L - hit
+    cu_r, out_r, init_r = (kda.IndexArray([0, rest], dev), kda.IndexArray([req], dev),
+                           kda.IndexArray([req], dev))
+    o_r = torch.empty((rest, H, D), dtype=torch.bfloat16, device=dev)
+    P = 9
+    vw = ki.verify_workload(31, B=1, P=P, H=H)
+    vt = vw["tokens"]
+    vq, vk, vv, va, vb = (x.to(dev).contiguous() for x in (vt.q, vt.k, vt.v, vt.a, vt.b))
+    vo = torch.empty((1, P, H, D), dtype=torch.bfloat16, device=dev)
+    sl, na = kda.IndexArray([req], dev), torch.from_numpy(vw["n_accepted"]).to(dev)
+    calls = [unal,
+             lambda: pool.kda_slot_checkpoint(cached, req),
+             lambda: pool.kda_prefill(q[hit:], k[hit:], v[hit:], a[hit:], b[hit:], cu_r, out_r,
+                                      init_slots=init_r, o=o_r),
+             lambda: pool.kda_verify(vq, vk, vv, va, vb, sl, o=vo),
+             lambda: pool.kda_commit(sl, na)]
+    for _ in range(2):
+        for fn in calls:
+            fn()
+    ms = [float(np.median(x)) for x in cold.time(iters, calls)]
+    served = ms[1] + ms[2] + ms[3] + ms[4]
+    res = {"workload": "one 8192-token prompt, H=32, d=128: checkpoints every 1000 tokens against "
+                       "every 1024; a 6144-token prefix-cache hit (checkpoint copy, prefill of the "
+                       "other 2048 tokens from it, verify of 1+8 drafts and commit on the slot)",
+           "unaligned_1000_ms": round(ms[0], 5), "aligned_1024_ms": aligned_ms,
+           "unaligned_over_aligned": round(ms[0] / aligned_ms, 3),
+           "hit": {"cached_tokens": hit, "checkpoint_copy_ms": round(ms[1], 5),
+                   "prefill_rest_ms": round(ms[2], 5), "verify_ms": round(ms[3], 5),
+                   "commit_ms": round(ms[4], 5), "served_ms": round(served, 5),
+                   "full_prefill_ms": aligned_ms, "served_over_full": round(served / aligned_ms, 3)}}
+    del pool
+    return res
+
+
 def bench_prefill(torch, kda, ki, dev, cold, iters):
     w = ki.prefill_workload(3)
     H, L, I = w["H"], w["cu_seqlens"][-1], w["ckpt_interval"]
@@ -576,6 +637,8 @@ def main():
                    "verify_schemes": bench_verify_schemes(torch, kda, ki, dev, cold,
                                                           max(args.config_iters // 5, 3)),
                    "prefill_8192": bench_prefill(torch, kda, ki, dev, cold, max(args.config_iters // 2, 1))}
+        configs["prefix_hit_and_intervals"] = bench_prefix_hit_and_intervals(
+            torch, kda, ki, dev, cold, max(args.config_iters // 5, 3), configs["prefill_8192"]["ms"])
         del cold
         peaks = measured_peaks(torch, dev)
         # each HBM-bound figure also as a share of what a plain device copy sustains
