@@ -205,7 +205,8 @@ kda_status kda_verify(kda_pool* pool, const kda_step_args* args, int32_t n_pos, 
  * accepted drafts n per sequence; 1 + n ring entries from v_base are replayed into the slot
  * with the same arithmetic as kda_decode (bit-identical to 1 + n decode calls), the state
  * is written once, ring_head = (v_base + 1 + n) mod ring_cap, pos += 1 + n, pending = 0.
- * n outside [0, v_npos - 1] sets KDA_DEVERR_NACC_RANGE and is clamped. Slots must be pending. */
+ * n outside [0, v_npos - 1] sets KDA_DEVERR_NACC_RANGE and is clamped. Slots must be pending.
+ * As for kda_decode, a batch of at most 64 takes its slot indices from h_slots.              */
 kda_status kda_commit(kda_pool* pool, int32_t B, const int32_t* h_slots,
                       const int32_t* d_slots, const int32_t* d_n_accepted, void* stream);
 

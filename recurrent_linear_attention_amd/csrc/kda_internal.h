@@ -57,14 +57,14 @@ struct PrefillLaunch {
   StatePlan plan;              // from plan_state_pass (host lengths)
 };
 
-// Decode takes the host copy of the slot indices too: a batch of at most SLOT_ARG_MAX
+// Decode and commit take the host copy of the slot indices too: a batch of at most SLOT_ARG_MAX
 // sequences passes them by value among the kernel arguments.
 constexpr int SLOT_ARG_MAX = 64;
 hipError_t launch_decode(const PoolView& p, const StepTensors& t, int32_t B, const int32_t* h_slots,
                          const int32_t* d_slots, hipStream_t s);
 hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int32_t n_pos,
                          const int32_t* d_slots, hipStream_t s);
-hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots,
+hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* h_slots, const int32_t* d_slots,
                          const int32_t* d_n_accepted, hipStream_t s);
 hipError_t launch_rollback(const PoolView& p, int32_t B, const int32_t* d_slots,
                            hipStream_t s);

@@ -431,7 +431,7 @@ kda_status kda_commit(kda_pool* p, int32_t B, const int32_t* h_slots, const int3
   if (st != KDA_OK) return st;
   if (B == 0) return KDA_OK;
   if (!d_slots || !d_n_accepted) return fail(KDA_EINVAL, "null device array");
-  hipError_t e = kda::launch_commit(p->view, B, d_slots, d_n_accepted, as_stream(stream));
+  hipError_t e = kda::launch_commit(p->view, B, h_slots, d_slots, d_n_accepted, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "commit launch");
   for (int32_t i = 0; i < B; ++i) p->slot_state[h_slots[i]] = SLOT_IDLE;
   return KDA_OK;
@@ -527,7 +527,7 @@ kda_status kda_mixed_batch(kda_pool* p, const kda_mixed_args* m, void* stream) {
     hipError_t run(hipStream_t on) const {
       hipError_t e = hipSuccess;
       if (m->n_commit > 0) {
-        e = kda::launch_commit(p->view, m->n_commit, m->d_commit_slots, m->d_n_accepted, on);
+        e = kda::launch_commit(p->view, m->n_commit, m->h_commit_slots, m->d_commit_slots, m->d_n_accepted, on);
         if (e != hipSuccess) return e;
       }
       if (m->n_decode > 0) {

@@ -286,10 +286,11 @@ __device__ __forceinline__ void stepped_positions(int n, float (&S)[C::RPT][4], 
   }
 }
 
-// Slot indices of a decode batch of at most SLOT_ARG_MAX sequences, by value among the kernel
-// arguments (decode_kernel<D, true>; larger batches read the device array). The kernel's
-// arguments are loaded before anything else, so the state tile's address then waits for no
-// load of its own (16 sequences, cold, by events: 21.8 -> 21.2 us).
+// Slot indices of a decode or commit batch of at most SLOT_ARG_MAX sequences, by value among the
+// kernel arguments (decode_kernel<D, true>, commit_kernel<D, true>; larger batches read the
+// device array). The kernel's arguments are loaded before anything else, so the state tile's
+// address then waits for no load of its own (decode of 16 sequences, cold, by events: 21.8 ->
+// 21.2 us).
 struct SlotArg {
   int32_t id[SLOT_ARG_MAX];
 };
@@ -726,15 +727,17 @@ __global__ __launch_bounds__(VC_NT) void verify_wy_kernel(PoolView P, StepTensor
   }
 }
 
-// ReplaySSM commit: replay 1 + n_accepted ring entries into the slot, store once.
-template <int D>
-__global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, const int32_t* __restrict__ slots,
+// ReplaySSM commit: replay 1 + n_accepted ring entries into the slot, store once. Grid and slot
+// ids as for decode_kernel (the sequence in y; ids by value for up to SLOT_ARG_MAX sequences).
+template <int D, bool BY_VALUE>
+__global__ __launch_bounds__(StepCfg<D>::NT) void commit_kernel(PoolView P, SlotArg sa,
+                                                                const int32_t* __restrict__ slots,
                                                                 const int32_t* __restrict__ n_acc) {
   using C = StepCfg<D>;
   __shared__ StepLds<C> lds;
   constexpr int NVS = D / C::VS;
-  const int vs = blockIdx.x % NVS, h = (blockIdx.x / NVS) % P.H, bi = blockIdx.x / (NVS * P.H);
-  const int slot = slots[bi];
+  const int vs = blockIdx.x % NVS, h = blockIdx.x / NVS, bi = blockIdx.y;
+  const int slot = BY_VALUE ? sa.id[bi] : slots[bi];
   if (slot < 0 || slot >= P.num_slots) {
     if (threadIdx.x == 0 && h == 0 && vs == 0) atomicOr(P.err, DEVERR_SLOT_RANGE);
     return;
@@ -915,12 +918,21 @@ hipError_t launch_verify(const PoolView& p, const StepTensors& t, int32_t B, int
   return hipGetLastError();
 }
 
-hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* d_slots, const int32_t* d_n_acc,
-                         hipStream_t s) {
-  if (p.dk == 128)
-    hipLaunchKernelGGL(commit_kernel<128>, dim3(step_blocks<128>(p, B)), dim3(StepCfg<128>::NT), 0, s, p, d_slots, d_n_acc);
+hipError_t launch_commit(const PoolView& p, int32_t B, const int32_t* h_slots, const int32_t* d_slots,
+                         const int32_t* d_n_acc, hipStream_t s) {
+  SlotArg sa{};
+  const bool by_value = B <= SLOT_ARG_MAX;
+  if (by_value)
+    for (int32_t i = 0; i < B; ++i) sa.id[i] = h_slots[i];
+  const dim3 g128(step_blocks<128>(p, 1), B), g16(step_blocks<16>(p, 1), B);
+  if (p.dk == 128 && by_value)
+    hipLaunchKernelGGL((commit_kernel<128, true>), g128, dim3(StepCfg<128>::NT), 0, s, p, sa, d_slots, d_n_acc);
+  else if (p.dk == 128)
+    hipLaunchKernelGGL((commit_kernel<128, false>), g128, dim3(StepCfg<128>::NT), 0, s, p, sa, d_slots, d_n_acc);
+  else if (by_value)
+    hipLaunchKernelGGL((commit_kernel<16, true>), g16, dim3(StepCfg<16>::NT), 0, s, p, sa, d_slots, d_n_acc);
   else
-    hipLaunchKernelGGL(commit_kernel<16>, dim3(step_blocks<16>(p, B)), dim3(StepCfg<16>::NT), 0, s, p, d_slots, d_n_acc);
+    hipLaunchKernelGGL((commit_kernel<16, false>), g16, dim3(StepCfg<16>::NT), 0, s, p, sa, d_slots, d_n_acc);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ hipError_t hipMemcpyAsync(void* dst, const void*, size_t n, hipMemcpyKind, hipSt
 namespace kda {
 hipError_t launch_decode(const PoolView&, const StepTensors&, int32_t, const int32_t*, const int32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_verify(const PoolView&, const StepTensors&, int32_t, int32_t, const int32_t*, hipStream_t) { return hipSuccess; }
-hipError_t launch_commit(const PoolView&, int32_t, const int32_t*, const int32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_commit(const PoolView&, int32_t, const int32_t*, const int32_t*, const int32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_rollback(const PoolView&, int32_t, const int32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_verify_direct(const PoolView&, const StepTensors&, int32_t, int32_t, const int32_t*, float*, hipStream_t) { return hipSuccess; }
 hipError_t launch_commit_direct(const PoolView&, int32_t, const int32_t*, const int32_t*, const float*, int32_t, hipStream_t) { return hipSuccess; }

@@ -143,6 +143,28 @@ def test_decode_slot_ids_by_value_and_from_device(d, B):
 
 # ----------------------------------------------------------------------------- verify / commit
 
+@pytest.mark.parametrize("d,B", [(128, 64), (128, 65), (16, 65)])
+def test_commit_slot_ids_by_value_and_from_device(d, B):
+    """Commit takes the slot ids of at most 64 sequences by value among the kernel arguments
+    and reads the device array beyond: a verify of 1+2 positions and the commit of random
+    accepted counts on both sides of that limit, state and metadata against the oracle."""
+    H, n_slots, P = 2, 96, 3
+    rng = np.random.default_rng(650 + B + d)
+    g, o = pools(n_slots, H, d, R=P)
+    slots = rng.permutation(n_slots)[:B].astype(np.int32)
+    put_states(g, o, slots, ki.draw_states(rng, B, H, d, d))
+    tok = ki.draw_tokens(rng, (B, P), H, d, d)
+    g.kda_verify(*tok_dev(tok), slots)
+    o.verify(tok.np, slots)
+    na = rng.integers(0, P, size=B).astype(np.int32)
+    g.kda_commit(slots, torch.from_numpy(na).to("cuda"))
+    o.commit(slots, na)
+    torch.cuda.synchronize()
+    check_state(g.state[slots.tolist()], o.state[slots])
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    assert device_errors(g) == 0
+
+
 def test_verify_commit_rollback_full_size():
     w = ki.verify_workload(2)
     g, o = pools(w["n_slots"], w["H"], w["dk"], w["ring_cap"])
