@@ -29,8 +29,8 @@ by heads over a process pool of the host's cores, before the GPU is touched.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 30]
 
-Before the W warm-up steps the step runs untimed for PREWARM_S seconds of wall clock (reported
-as `prewarm`): an idle GPU raises its clock only under sustained load, and a few warm-up steps
+Before the W warm-up steps the step runs PREWARM_STEPS times untimed (~0.3 s; reported as
+`prewarm`): an idle GPU raises its clock only under sustained load, and a few warm-up steps
 alone leave the timed steps up to ~10% slow. The timed steps then measure the steady serving
 rate.
 """
@@ -49,7 +49,7 @@ METRIC = "KDA tokens/s + achieved HBM GB/s (decode/verify), MFMA % (prefill), 1 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16
 DTYPE = "bf16 q/k/v/o, fp16 matrix-core operands, fp32 state and accumulation"
-PREWARM_S = 0.3                 # untimed steps before the warm-up steps (s of wall clock)
+PREWARM_STEPS = 700             # untimed steps before the warm-up steps (~0.3 s)
 
 # Algorithmic bytes (d = 128, fp32 state, bf16 q/k/v/o, fp32 a and b).
 D = 128
@@ -562,12 +562,11 @@ def main():
                              n_accepted=na)
 
     print("bench: mixed step ...", file=sys.stderr, flush=True)
-    n_pre_warm, t_pw = 0, time.perf_counter()
-    while time.perf_counter() - t_pw < PREWARM_S:
-        for _ in range(16):
-            step()
-        torch.cuda.synchronize()
-        n_pre_warm += 16
+    t_pw = time.perf_counter()
+    for _ in range(PREWARM_STEPS):
+        step()
+    torch.cuda.synchronize()
+    s_pre_warm = time.perf_counter() - t_pw
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -651,7 +650,7 @@ def main():
 
     out = {"metric": METRIC, "value": round(total_tok / (ms_step / 1e3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "prewarm": {"steps": n_pre_warm, "s": PREWARM_S},
+           "prewarm": {"steps": PREWARM_STEPS, "s": round(s_pre_warm, 3)},
            "ms_per_step": round(ms_step, 4), "ms_per_step_device": round(ms_step_dev, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
            "data": "synthetic (seeded, kda_inputs)",
