@@ -89,6 +89,33 @@ class IndexArray:
         return self.dev.data_ptr() if self.np.size else None
 
 
+class _StreamEvent:
+    """A HIP event for ordering streams of one device: created through the HIP runtime torch
+    loaded (the one libkda.so binds to) with hipEventDisableTiming | hipEventDisableSystemFence,
+    destroyed with its owner."""
+    _hip = None
+    FLAGS = 0x2 | 0x20000000
+
+    def __init__(self):
+        if _StreamEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(c_void_p), ctypes.c_uint]
+            hip.hipEventCreateWithFlags.restype = ctypes.c_int
+            hip.hipEventDestroy.argtypes = [c_void_p]
+            hip.hipEventDestroy.restype = ctypes.c_int
+            _StreamEvent._hip = hip
+        h = c_void_p()
+        err = _StreamEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), self.FLAGS)
+        if err != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({err})")
+        self.handle = h.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _StreamEvent._hip is not None:
+            _StreamEvent._hip.hipEventDestroy(self.handle)
+            self.handle = None
+
+
 class KDAPool:
     """A pool of fp32 KDA state slots with per-slot ReplaySSM rings, on one GPU."""
 
@@ -317,18 +344,17 @@ class KDAPool:
         return o
 
     def _side_stream(self):
-        """Side stream (default priority) and fork / join events for mixed batches, from torch.
-        torch creates an event's HIP handle when it is first recorded, so both are recorded once
-        here before their handles are passed on."""
+        """Side stream (default priority, from torch) and fork / join events for mixed batches.
+        The events only order two streams of one device, so they are made without timing and
+        without the system-scope fence an event record otherwise performs (a cache write-back
+        for the host's sake: ~3 us per mixed step)."""
         if self._side is None:
             side = torch.cuda.Stream(device=self.device)
-            evs = [torch.cuda.Event(), torch.cuda.Event()]
-            for e in evs:
-                e.record(side)
-            side.synchronize()
+            with torch.cuda.device(self.device):
+                evs = [_StreamEvent(), _StreamEvent()]
             self._side = (side, evs)
         side, evs = self._side
-        return side, evs[0].cuda_event, evs[1].cuda_event
+        return side, evs[0].handle, evs[1].handle
 
     def kda_prefill_plan(self, cu_seqlens) -> list:
         """Width plan of kda_prefill's state pass for these sequence boundaries:

@@ -1123,6 +1123,57 @@ def test_mixed_batch_commits_previous_verify(d):
     assert device_errors(g) == 0
 
 
+def test_mixed_batches_hand_slots_between_streams():
+    """Two mixed batches enqueued back to back with no host synchronisation between them, each
+    stream reading what the other wrote in the batch before: the second batch decodes the slots
+    the first one prefilled (caller's stream, then side stream: ordered by the fork event),
+    resumes prefills from the slots the first one decoded (side stream, then caller's stream:
+    ordered by the join event), and commits and re-verifies the first one's verified slot.
+    Outputs, states and metadata against the oracle applying the same operations in order."""
+    H, d, P = 4, 128, 5
+    g, o = pools(32, H, d)
+    rng = np.random.default_rng(95)
+    ds1, vs1 = [10, 11], [20]
+    put_states(g, o, ds1 + vs1, ki.draw_states(rng, 3, H, d, d))
+
+    def cu_of(lens):
+        return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+    def parts(tok, n_pre, nd, nv):
+        vt = {n: x[n_pre + nd:].reshape((nv, P) + x.shape[1:]) for n, x in tok.np.items()}
+        return tok.slice(0, n_pre).np, tok.slice(n_pre, n_pre + nd).np, vt
+
+    cu1, out1 = cu_of([300, 150]), [0, 1]
+    n1 = int(cu1[-1])
+    tok1 = ki.draw_tokens(rng, (n1 + len(ds1) + len(vs1) * P,), H, d, d)
+    O1 = g.kda_mixed_batch(*tok_dev(tok1), cu1, out1, ds1, vs1, P)
+    cu2, init2, out2, ds2, vs2 = cu_of([200, 70]), [10, 11], [12, 13], [0, 1], [20]
+    n2 = int(cu2[-1])
+    na = [2]
+    tok2 = ki.draw_tokens(rng, (n2 + len(ds2) + len(vs2) * P,), H, d, d)
+    O2 = g.kda_mixed_batch(*tok_dev(tok2), cu2, out2, ds2, vs2, P, init_slots=init2,
+                           commit_slots=vs2, n_accepted=torch.tensor(na, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+    p1, d1, v1 = parts(tok1, n1, len(ds1), len(vs1))
+    Op1, Od1, Ov1 = o.prefill(p1, cu1, [-1, -1], out1, [], 0), o.decode(d1, ds1), o.verify(v1, vs1)
+    o.commit(vs2, na)
+    p2, d2, v2 = parts(tok2, n2, len(ds2), len(vs2))
+    Op2, Od2, Ov2 = o.prefill(p2, cu2, init2, out2, [], 0), o.decode(d2, ds2), o.verify(v2, vs2)
+    for O, n, cu, Op, Od, Ov, tok, nd in ((O1, n1, cu1, Op1, Od1, Ov1, tok1, len(ds1)),
+                                          (O2, n2, cu2, Op2, Od2, Ov2, tok2, len(ds2))):
+        vv = tok.np["v"]
+        check_out(O[:n], Op, cu, v=vv[:n])
+        check_out(O[n:n + nd], Od, v=vv[n:n + nd])
+        check_out(O[n + nd:].reshape(1, P, H, d), Ov, v=vv[n + nd:].reshape(1, P, H, d))
+    touched = out1 + ds1 + vs1 + out2
+    for s_ in touched:
+        check_state(g.state[s_], o.state[s_])
+    meta_equal(g.meta_array(), o.meta(), touched)
+    ring_check(g, o, vs2)
+    assert device_errors(g) == 0
+
+
 def test_mixed_batch_is_deterministic():
     """The same mixed batch (prefill on the caller's stream, commit / decode / verify on the
     side stream) on two pools with the same contents gives the same bytes: outputs, states,
