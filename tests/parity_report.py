@@ -1,7 +1,7 @@
 """Summarise the measured parity errors that the GPU tests append to KDA_PARITY_LOG.
 
-    KDA_PARITY_LOG=gpurun_out/parity_margins.jsonl python -m pytest tests -m gpu
-    python tests/parity_report.py gpurun_out/parity_margins.jsonl > profiles/parity_margins.md
+    KDA_PARITY_LOG=/tmp/parity_margins.jsonl python -m pytest tests -m gpu
+    python tests/parity_report.py /tmp/parity_margins.jsonl > profiles/parity_margins.md
 
 One row per test: the worst error over its checks of bf16 outputs (rel_bf16) and of fp32
 states (rel), each over the whole tensor and per (sequence, head), against the 2e-3 bound.
