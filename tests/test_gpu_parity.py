@@ -945,6 +945,54 @@ def test_mixed_batch_without_side_stream_matches_forked():
     assert np.array_equal(M1, M2)
 
 
+@pytest.mark.parametrize("d,H", [(128, 3), (128, 5), (16, 5), (16, 1)])
+def test_odd_head_counts_through_every_path(d, H):
+    """Head counts that are not a multiple of the eight XCDs (the state pass rounds each width
+    group's grid up and idles the spare work-groups; the step kernels tile heads by slot):
+    a mixed batch (three ragged prompts, one resumed, checkpoints; decodes; verifies of 1+4),
+    then the verifies' commit and a decode of the committed slots, each against the oracle."""
+    P, interval = 5, (128 if d == 128 else 32)
+    rng = np.random.default_rng(400 + 10 * H + d)
+    lens = [200, 67, 130] if d == 128 else [50, 17, 33]
+    ds, vs = [3, 4], [6, 7, 8]
+    n_ck = sum(L // interval for L in lens)
+    n_slots = 10 + n_ck
+    g, o = pools(n_slots, H, d, P)
+    put_states(g, o, ds + vs + [9], ki.draw_states(rng, 6, H, d, d))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    out, init = [0, 1, 2], [9, -1, -1]
+    cks = list(range(10, 10 + n_ck))
+    n_pre = int(cu[-1])
+    tok = ki.draw_tokens(rng, (n_pre + len(ds) + len(vs) * P,), H, d, d)
+    O = g.kda_mixed_batch(*tok_dev(tok), cu, out, ds, vs, P, init_slots=init, ckpt_slots=cks,
+                          ckpt_interval=interval)
+    torch.cuda.synchronize()
+    Op = o.prefill(tok.slice(0, n_pre).np, cu, init, out, cks, interval)
+    Od = o.decode(tok.slice(n_pre, n_pre + len(ds)).np, ds)
+    vt = {n: x[n_pre + len(ds):].reshape((len(vs), P) + x.shape[1:]) for n, x in tok.np.items()}
+    Ov = o.verify(vt, vs)
+    check_out(O[:n_pre], Op, cu, v=tok.np["v"][:n_pre])
+    check_out(O[n_pre:n_pre + len(ds)], Od, v=tok.np["v"][n_pre:n_pre + len(ds)])
+    check_out(O[n_pre + len(ds):].reshape(len(vs), P, H, d), Ov,
+              v=tok.np["v"][n_pre + len(ds):].reshape(len(vs), P, H, d))
+    for s in out + cks + ds:
+        check_state(g.state[s], o.state[s])
+    ring_check(g, o, vs)
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    na = np.array([4, 0, 2], dtype=np.int32)
+    g.kda_commit(vs, torch.from_numpy(na).to("cuda"))
+    o.commit(vs, na)
+    t2 = ki.draw_tokens(rng, (len(vs),), H, d, d)
+    O2 = g.kda_decode(*tok_dev(t2), vs)
+    O2o = o.decode(t2.np, vs)
+    torch.cuda.synchronize()
+    check_out(O2, O2o, v=t2.np["v"])
+    for s in vs:
+        check_state(g.state[s], o.state[s])
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    assert device_errors(g) == 0
+
+
 def test_mixed_batch_without_prefill():
     """Only decode and verify parts: they run on the caller's stream, as separate calls would."""
     H, d, P = 4, 128, 5
