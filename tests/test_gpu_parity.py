@@ -1299,3 +1299,71 @@ def test_slot_reset_and_checkpoint_copy():
     assert torch.equal(g.state[7], g.state[2])
     assert not g.state[5].any()
     meta_equal(g.meta_array(), o.meta(), [2, 5, 7])
+
+
+# ----------------------------------------------------------------------------- large pool
+
+def test_large_pool_high_slot_indices():
+    """An 8192-slot pool at H = 32, d = 128 (16 GiB of fp32 state, 2.4 GB of ring): decode,
+    verify of 1+8 and its commit, a resumed prefill with in-pass checkpoints, and a slot
+    checkpoint copy, on slots whose state lies past 2^31 floats and 2^31 bytes of the pool,
+    against the oracle on a compact pool holding the same slots' contents."""
+    H, d, n, R = 32, 128, 8192, 9
+    g = kda.KDAPool(n, H, d, R)
+    for _ in range(n):
+        g.kda_slot_alloc()
+    dec, ver, pre_init = [8191, 6000, 4100], [8190, 5001], 6001
+    pre_out, cks, cp_dst = [8189, 4099], [8100, 8101, 8102], 100
+    used = dec + ver + [pre_init] + pre_out + cks + [cp_dst]
+    m = {s: i for i, s in enumerate(used)}
+    o = OPool(len(used), H, d, d, R)
+    for _ in used:
+        o.alloc()
+    om = lambda slots: [m[s] for s in slots]  # noqa: E731
+    rng = np.random.default_rng(8192)
+    seeded = dec + ver + [pre_init]
+    st = ki.draw_states(rng, len(seeded), H, d, d)
+    g.state[seeded] = st.to("cuda")
+    o.state[om(seeded)] = st.double().numpy()
+
+    def same_meta(slots):
+        np.testing.assert_array_equal(g.meta_array()[slots], o.meta()[om(slots)])
+
+    tok = ki.draw_tokens(rng, (len(dec),), H, d, d)
+    O = g.kda_decode(*tok_dev(tok), dec)
+    Oo = o.decode(tok.np, om(dec))
+    torch.cuda.synchronize()
+    check_out(O, Oo, v=tok.np["v"])
+    for s in dec:
+        check_state(g.state[s], o.state[m[s]])
+
+    P = 9
+    vt = ki.draw_tokens(rng, (len(ver), P), H, d, d)
+    Ov = g.kda_verify(*tok_dev(vt), ver)
+    Ovo = o.verify(vt.np, om(ver))
+    torch.cuda.synchronize()
+    check_out(Ov, Ovo, v=vt.np["v"])
+    na = np.array([8, 3], dtype=np.int32)
+    g.kda_commit(ver, torch.from_numpy(na).to("cuda"))
+    o.commit(om(ver), na)
+    torch.cuda.synchronize()
+    for s in ver:
+        check_state(g.state[s], o.state[m[s]])
+
+    lens, interval = [700, 300], 256
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pt = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    Op = g.kda_prefill(*tok_dev(pt), cu, pre_out, init_slots=[pre_init, -1], ckpt_slots=cks,
+                       ckpt_interval=interval)
+    Opo = o.prefill(pt.np, cu, [m[pre_init], -1], om(pre_out), om(cks), interval)
+    torch.cuda.synchronize()
+    check_out(Op, Opo, cu, v=pt.np["v"])
+    for s in pre_out + cks:
+        check_state(g.state[s], o.state[m[s]])
+
+    g.kda_slot_checkpoint(8189, cp_dst)
+    o.checkpoint(m[8189], m[cp_dst])
+    torch.cuda.synchronize()
+    assert torch.equal(g.state[cp_dst], g.state[8189])
+    same_meta(used)
+    assert device_errors(g) == 0
