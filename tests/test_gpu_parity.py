@@ -1367,3 +1367,33 @@ def test_large_pool_high_slot_indices():
     assert torch.equal(g.state[cp_dst], g.state[8189])
     same_meta(used)
     assert device_errors(g) == 0
+
+
+def test_prefill_long_prompt():
+    """One 65536-token prompt (1024 chunks in one chain) at H = 8, resumed from a slot, with a
+    checkpoint every 8192 tokens: outputs, the 8 checkpoints and the final state of two heads
+    against the oracle, every head finite."""
+    H, d, L, interval = 8, 128, 65536, 8192
+    rng = np.random.default_rng(65536)
+    n_ck = L // interval
+    g, _ = pools(n_ck + 2, H, d)
+    cu = np.array([0, L], dtype=np.int32)
+    init, out, cks = n_ck + 1, 0, list(range(1, n_ck + 1))
+    st = ki.draw_states(rng, 1, H, d, d)
+    g.state[init] = st[0].to("cuda")
+    tok = ki.draw_tokens(rng, (L,), H, d, d)
+    O = g.kda_prefill(*tok_dev(tok), cu, [out], init_slots=[init], ckpt_slots=cks,
+                      ckpt_interval=interval)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all() and torch.isfinite(g.state[[out] + cks]).all()
+    heads = [0, 5]
+    o = OPool(n_ck + 2, len(heads), d, d, 9)
+    for _ in range(n_ck + 2):
+        o.alloc()
+    o.state[init] = st[0][heads].double().numpy()
+    Oo = o.prefill(heads_np(tok, heads), cu, [init], [out], cks, interval)
+    check_out(O[:, heads], Oo, cu, v=tok.np["v"][:, heads])
+    for s in [out] + cks:
+        check_state(g.state[s][heads], o.state[s])
+    assert torch.equal(g.state[cks[-1]], g.state[out])   # the last boundary is the prompt's end
+    assert device_errors(g) == 0
