@@ -222,7 +222,8 @@ class TimingEvent:
     def __init__(self, torch, enable_timing=True):
         import ctypes
         if TimingEvent._hip is None:
-            hip = ctypes.CDLL("libamdhip64.so.7")
+            from recurrent_linear_attention_amd import _abi
+            hip = _abi.hip_runtime()
             hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

@@ -99,15 +99,29 @@ PROTOTYPES = {
 }
 
 
-def _check_single_runtime() -> None:
+def _mapped_hip_runtimes() -> set[str]:
     try:
         maps = open("/proc/self/maps").read().splitlines()
     except OSError:
-        return
-    hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+        return set()
+    return {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+
+
+def _check_single_runtime() -> None:
+    hip = _mapped_hip_runtimes()
     if len(hip) > 1:
         raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(sorted(hip))
                           + "); import torch before loading libkda.so")
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime this process already holds (the one torch loaded and libkda.so binds
+    to), opened by its mapped path, so that events created through it belong to the same
+    runtime as torch's streams."""
+    hip = _mapped_hip_runtimes()
+    if len(hip) != 1:
+        raise RuntimeError(f"expected one mapped HIP runtime, found {sorted(hip)}")
+    return ctypes.CDLL(next(iter(hip)))
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:

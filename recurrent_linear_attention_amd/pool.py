@@ -98,7 +98,7 @@ class _StreamEvent:
 
     def __init__(self):
         if _StreamEvent._hip is None:
-            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip = _abi.hip_runtime()
             hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(c_void_p), ctypes.c_uint]
             hip.hipEventCreateWithFlags.restype = ctypes.c_int
             hip.hipEventDestroy.argtypes = [c_void_p]
