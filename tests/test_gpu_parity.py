@@ -1397,3 +1397,74 @@ def test_prefill_long_prompt():
         check_state(g.state[s][heads], o.state[s])
     assert torch.equal(g.state[cks[-1]], g.state[out])   # the last boundary is the prompt's end
     assert device_errors(g) == 0
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_mixed_batches_random_shapes(seed):
+    """Two serving steps of mixed batches with shapes drawn at random: head count 1-8, d = 16
+    or 128, 0-4 prompts of 0-300 tokens (some resumed from a slot, checkpoints at a random
+    interval), 0-4 decodes, 1-3 verifies of 1-9 positions; the second step commits the first
+    one's verifies with random accepted counts and verifies some of those slots again. Every
+    output, state, ring entry and metadata field against the oracle after each step."""
+    rng = np.random.default_rng(9000 + seed)
+    d = int(rng.choice([16, 128]))
+    H = int(rng.integers(1, 9))
+    P = int(rng.integers(1, 10))
+    R = max(P, 9)
+    n_slots = 192   # 12 seeded, and per step up to 4 out slots and 72 checkpoint slots
+    g, o = pools(n_slots, H, d, R)
+    free = list(rng.permutation(n_slots))
+    take = lambda n: [int(free.pop()) for _ in range(n)]  # noqa: E731
+    seeded = take(12)
+    st = ki.draw_states(rng, len(seeded), H, d, d)
+    put_states(g, o, seeded, st)
+    verify_slots = seeded[:int(rng.integers(1, 4))]
+    rest = seeded[len(verify_slots):]
+
+    def step(commit=None):
+        n_seq = int(rng.integers(0, 5))
+        lens = [int(x) for x in rng.integers(0, 301, size=n_seq)]
+        interval = int(rng.choice([0, 16, 37, 64, 100]))
+        n_ck = sum(L // interval for L in lens) if interval else 0
+        out, cks = take(n_seq), take(n_ck)
+        init = [int(rest.pop()) if (rest and rng.random() < 0.5) else -1 for _ in range(n_seq)]
+        dec = [s for s in rest[:int(rng.integers(0, 5))]]
+        for s in dec:
+            rest.remove(s)
+        ver = verify_slots if commit is None else [s for s in verify_slots if rng.random() < 0.7] or verify_slots[:1]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        n_pre = int(cu[-1])
+        tok = ki.draw_tokens(rng, (n_pre + len(dec) + len(ver) * P,), H, d, d)
+        kw = {}
+        if commit is not None:
+            kw = dict(commit_slots=commit[0], n_accepted=torch.from_numpy(commit[1]).to("cuda"))
+            o.commit(commit[0], commit[1])
+        O = g.kda_mixed_batch(*tok_dev(tok), cu, out, dec, ver, P, init_slots=init,
+                              ckpt_slots=cks, ckpt_interval=interval, **kw)
+        torch.cuda.synchronize()
+        if n_seq:
+            Op = o.prefill(tok.slice(0, n_pre).np, cu, init, out, cks, interval)
+            check_out(O[:n_pre], Op, cu, v=tok.np["v"][:n_pre])
+        if dec:
+            Od = o.decode(tok.slice(n_pre, n_pre + len(dec)).np, dec)
+            check_out(O[n_pre:n_pre + len(dec)], Od, v=tok.np["v"][n_pre:n_pre + len(dec)])
+        vt = {n: x[n_pre + len(dec):].reshape((len(ver), P) + x.shape[1:]) for n, x in tok.np.items()}
+        Ov = o.verify(vt, ver)
+        check_out(O[n_pre + len(dec):].reshape(len(ver), P, H, d), Ov,
+                  v=tok.np["v"][n_pre + len(dec):].reshape(len(ver), P, H, d))
+        for s in out + cks + dec + (commit[0] if commit is not None else []):
+            check_state(g.state[s], o.state[s])
+        ring_check(g, o, ver)
+        meta_equal(g.meta_array(), o.meta(), range(n_slots))
+        return ver
+
+    ver1 = step()
+    na = rng.integers(0, P, size=len(ver1)).astype(np.int32)
+    ver2 = step(commit=(ver1, na))
+    g.kda_commit(ver2, torch.from_numpy(np.zeros(len(ver2), dtype=np.int32)).to("cuda"))
+    o.commit(ver2, np.zeros(len(ver2), dtype=np.int32))
+    torch.cuda.synchronize()
+    for s in ver2:
+        check_state(g.state[s], o.state[s])
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    assert device_errors(g) == 0
