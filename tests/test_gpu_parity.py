@@ -1468,3 +1468,45 @@ def test_mixed_batches_random_shapes(seed):
         check_state(g.state[s], o.state[s])
     meta_equal(g.meta_array(), o.meta(), range(n_slots))
     assert device_errors(g) == 0
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_batches(seed):
+    """Prefill batches drawn at random: 1-100 sequences of lognormal lengths (some empty, some
+    one chunk, a few thousand tokens), head count 1-8 (so the width plan varies from one width
+    for all to several groups, inside and outside the operand kernel's own plan), resumed
+    sequences, and a random checkpoint interval (0, aligned or not to the chunk), at d = 128 and
+    16: outputs, final and checkpoint states against the oracle, metadata exact. Total work is
+    bounded so that the oracle takes about a second."""
+    rng = np.random.default_rng(7000 + seed)
+    d = 128 if seed % 4 else 16
+    H = int(rng.integers(1, 9))
+    n_seq = int(rng.choice([1, 2, 5, 9, 40, 64, 65, 100]))
+    budget = 24000 // H
+    lengths = np.minimum(rng.lognormal(5.0, 1.2, size=n_seq).astype(int), 3000)
+    lengths[rng.random(n_seq) < 0.1] = 0
+    while lengths.sum() > budget:
+        lengths = lengths // 2
+    lengths = [int(x) for x in lengths]
+    interval = int(rng.choice([0, 64, 128, 100, 37]))
+    n_ck = sum(L // interval for L in lengths) if interval else 0
+    n_slots = 2 * n_seq + n_ck
+    g, o = pools(n_slots, H, d)
+    init = [i if rng.random() < 0.3 else -1 for i in range(n_seq)]
+    put_states(g, o, range(n_seq), ki.draw_states(rng, n_seq, H, d, d))
+    out = list(range(n_seq, 2 * n_seq))
+    cks = list(range(2 * n_seq, n_slots))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    tok = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+    if d == 128:
+        plan = g.kda_prefill_plan(cu)
+        assert plan[-1][0] == n_seq and all(w in (16, 32, 64, 128) for _, w in plan)
+    O = g.kda_prefill(*tok_dev(tok), cu, out, init_slots=init, ckpt_slots=cks,
+                      ckpt_interval=interval)
+    torch.cuda.synchronize()
+    Oo = o.prefill(tok.np, cu, init, out, cks, interval)
+    check_out(O, Oo, cu, v=tok.np["v"])
+    for s_ in out + cks:
+        check_state(g.state[s_], o.state[s_])
+    meta_equal(g.meta_array(), o.meta(), range(n_slots))
+    assert device_errors(g) == 0
