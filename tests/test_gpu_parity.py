@@ -1510,3 +1510,121 @@ def test_prefill_random_batches(seed):
         check_state(g.state[s_], o.state[s_])
     meta_equal(g.meta_array(), o.meta(), range(n_slots))
     assert device_errors(g) == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_operation_sequences(seed):
+    """40 pool operations drawn at random over a 10-slot pool, each on slots in the state it
+    needs: decode, verify + commit or rollback (ring scheme), verify_direct + commit_direct or
+    rollback (whole batches), slot reset, slot checkpoint copy, and a small resumed prefill.
+    After every operation its outputs, draft states and touched states are checked against the
+    oracle, ring entries and every slot's metadata exactly; the oracle then takes the GPU's
+    states, so each operation is checked from identical inputs."""
+    rng = np.random.default_rng(5100 + seed)
+    d = 16 if seed % 3 == 0 else 128
+    H, n, R = int(rng.integers(1, 5)), 10, 9
+    g, o = pools(n, H, d, R)
+    put_states(g, o, range(n), ki.draw_states(rng, n, H, d, d))
+    IDLE, RING, DIRECT = 1, 2, 3
+    state = {s: IDLE for s in range(n)}
+    npos, direct = {}, []
+
+    def idle(k):
+        c = [s for s in range(n) if state[s] == IDLE]
+        k = min(k, len(c))
+        return [int(x) for x in rng.choice(c, size=k, replace=False)] if k else []
+
+    ran = []
+
+    def sync(slots):
+        ran.append(len(slots))
+        torch.cuda.synchronize()
+        for s in slots:
+            check_state(g.state[s], o.state[s])
+            o.state[s] = f64(g.state[s])
+        meta_equal(g.meta_array(), o.meta(), range(n))
+
+    for _ in range(40):
+        op = rng.choice(["decode", "verify", "commit", "rollback", "vdirect", "cdirect",
+                         "reset", "copy", "prefill"])
+        if op == "decode" and idle(1):
+            S = idle(int(rng.integers(1, 4)))
+            t = ki.draw_tokens(rng, (len(S),), H, d, d)
+            O = g.kda_decode(*tok_dev(t), S)
+            check_out(O, o.decode(t.np, S), v=t.np["v"])
+            sync(S)
+        elif op in ("verify", "vdirect") and idle(1):
+            S, P = idle(int(rng.integers(1, 4))), int(rng.integers(1, R + 1))
+            t = ki.draw_tokens(rng, (len(S), P), H, d, d)
+            if op == "verify":
+                O = g.kda_verify(*tok_dev(t), S)
+                Oo = o.verify(t.np, S)
+                for s in S:
+                    state[s], npos[s] = RING, P
+            else:
+                O, dr = g.kda_verify_direct(*tok_dev(t), S)
+                Oo, dro = o.verify_direct(t.np, S)
+                torch.cuda.synchronize()
+                for b in range(len(S)):
+                    for j in range(P):
+                        check_state(dr[b, j], dro[b, j])
+                for s in S:
+                    state[s] = DIRECT
+                direct.append((S, P, dr))
+            torch.cuda.synchronize()
+            check_out(O, Oo, v=t.np["v"])
+            if op == "verify":
+                ring_check(g, o, S)
+            sync(S)
+        elif op == "commit" and any(v == RING for v in state.values()):
+            S = [s for s in range(n) if state[s] == RING and rng.random() < 0.7] or \
+                [s for s in range(n) if state[s] == RING][:1]
+            na = np.array([int(rng.integers(0, npos[s])) for s in S], dtype=np.int32)
+            g.kda_commit(S, torch.from_numpy(na).to("cuda"))
+            o.commit(S, na)
+            for s in S:
+                state[s] = IDLE
+            sync(S)
+        elif op == "cdirect" and direct:
+            S, P, dr = direct.pop(int(rng.integers(0, len(direct))))
+            na = rng.integers(0, P, size=len(S)).astype(np.int32)
+            g.kda_commit_direct(S, torch.from_numpy(na).to("cuda"), dr)
+            o.commit_direct(S, na, np.stack([f64(dr[b]) for b in range(len(S))]))
+            for s in S:
+                state[s] = IDLE
+            sync(S)
+        elif op == "rollback" and (direct or any(v == RING for v in state.values())):
+            if direct and rng.random() < 0.5:
+                S = direct.pop(int(rng.integers(0, len(direct))))[0]
+            else:
+                S = [s for s in range(n) if state[s] == RING][:int(rng.integers(1, 4))]
+                if not S:
+                    S = direct.pop()[0]
+            g.kda_rollback(S)
+            o.rollback(S)
+            for s in S:
+                state[s] = IDLE
+            sync(S)
+        elif op == "reset" and idle(1):
+            s = idle(1)[0]
+            g.kda_slot_reset(s)
+            o.reset(s)
+            sync([s])
+        elif op == "copy" and len(idle(2)) == 2:
+            src, dst = idle(2)
+            g.kda_slot_checkpoint(src, dst)
+            o.checkpoint(src, dst)
+            sync([dst])
+        elif op == "prefill" and len(idle(3)) == 3:
+            S = idle(3)
+            lens = [int(x) for x in rng.integers(0, 150, size=2)]
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            init, out = [S[2], -1], S[:2]
+            t = ki.draw_tokens(rng, (int(cu[-1]),), H, d, d)
+            O = g.kda_prefill(*tok_dev(t), cu, out, init_slots=init)
+            Oo = o.prefill(t.np, cu, init, out, [], 0)
+            torch.cuda.synchronize()
+            check_out(O, Oo, cu, v=t.np["v"])
+            sync(out)
+    assert len(ran) >= 25, f"only {len(ran)} of 40 drawn operations applied"
+    assert device_errors(g) == 0
