@@ -28,6 +28,10 @@
  *     no device work and changes no host state. KDA_EHIP means a HIP runtime call failed; part
  *     of the call's work may have been enqueued by then.
  *   - One pool is driven from one host thread at a time.
+ *   - Apart from kda_read_device_error, a call enqueues only kernel launches (and, for a mixed
+ *     batch with a side stream, the event record / wait pairs of its fork and join), so it can
+ *     be captured into a HIP graph; replaying the graph repeats the device work only (the
+ *     host-side slot states change once, at capture).
  *   - Supported shapes: dk == dv in {16, 128}; prefill chunk 16 (dk 16) or 64 (dk 128).
  *     Both prefill shapes run the chunked form on the matrix cores.
  */

@@ -1628,3 +1628,96 @@ def test_random_operation_sequences(seed):
             sync(out)
     assert len(ran) >= 25, f"only {len(ran)} of 40 drawn operations applied"
     assert device_errors(g) == 0
+
+
+@pytest.mark.parametrize("d", [128, 16])
+def test_steps_replayed_from_a_captured_graph(d):
+    """Decode, then verify of 1+4 and its commit, captured once into a HIP graph (torch.cuda.graph
+    on the binding's calls; slot arrays, accepted counts and outputs built before the capture)
+    and replayed four times, with eager work and a synchronisation between replays: after every
+    replay the outputs, states, rings and metadata equal, bit for bit, those of a second pool
+    that made the same calls eagerly as many times."""
+    H, P = 4, 5
+    rng = np.random.default_rng(31 + d)
+    pools_ = [pools(8, H, d)[0] for _ in range(2)]
+    st = ki.draw_states(rng, 8, H, d, d)
+    for g in pools_:
+        g.state.copy_(st.to("cuda"))
+    dec, ver = kda.IndexArray([1, 6], "cuda"), kda.IndexArray([2, 5], "cuda")
+    na = torch.tensor([3, 1], dtype=torch.int32, device="cuda")
+    td = tok_dev(ki.draw_tokens(rng, (2,), H, d, d))
+    tv = tok_dev(ki.draw_tokens(rng, (2, P), H, d, d))
+    outs = [(torch.empty((2, H, d), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((2, P, H, d), dtype=torch.bfloat16, device="cuda")) for _ in range(2)]
+
+    def calls(g, od, ov):
+        g.kda_decode(*td, dec, o=od)
+        g.kda_verify(*tv, ver, o=ov)
+        g.kda_commit(ver, na)
+
+    eager, graphed = pools_
+    calls(graphed, *outs[1])             # once eagerly on both pools before the capture
+    calls(eager, *outs[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):        # recorded, not run: both pools stay one step in
+        calls(graphed, *outs[1])
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(4):
+        graph.replay()
+        calls(eager, *outs[0])
+        scratch.add_(1.0)                # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(outs[1][0], outs[0][0]) and torch.equal(outs[1][1], outs[0][1])
+        assert torch.equal(graphed.state, eager.state)
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(graphed.ring_tensors(), eager.ring_tensors()))
+        assert np.array_equal(graphed.meta_array(), eager.meta_array())
+    assert device_errors(graphed) == 0 and device_errors(eager) == 0
+
+
+def test_mixed_step_replayed_from_a_captured_graph():
+    """A serving step through kda_mixed_batch (commit of the previous step's verifies, decodes,
+    verifies of 1+4, three prompts; commit, decode and verify forked to the binding's side
+    stream and joined back) captured into a HIP graph and replayed three times, with eager work
+    and a synchronisation between replays: after every replay outputs, states, rings and
+    metadata equal, bit for bit, those of a second pool stepping eagerly."""
+    H, d, P = 4, 128, 5
+    rng = np.random.default_rng(57)
+    st = ki.draw_states(rng, 10, H, d, d)
+    lens = [300, 129, 64]
+    cu = kda.IndexArray(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), "cuda")
+    out, dec, ver = (kda.IndexArray(x, "cuda") for x in ([0, 1, 2], [3, 4], [6, 7]))
+    n_tok = sum(lens) + 2 + 2 * P
+    tok = tok_dev(ki.draw_tokens(rng, (n_tok,), H, d, d))
+    na = torch.tensor([2, 4], dtype=torch.int32, device="cuda")
+    pools_ = []
+    for _ in range(2):
+        g = pools(10, H, d)[0]
+        g.state.copy_(st.to("cuda"))
+        o = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device="cuda")
+        g.kda_mixed_batch(*tok, cu, out, dec, ver, P, o=o)   # first step: nothing to commit
+        pools_.append((g, o))
+    (eager, oe), (graphed, og) = pools_
+
+    def step(g, o):
+        g.kda_mixed_batch(*tok, cu, out, dec, ver, P, o=o, commit_slots=ver, n_accepted=na)
+
+    step(eager, oe)
+    step(graphed, og)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(graphed, og)
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        graph.replay()
+        step(eager, oe)
+        scratch.mul_(0.5)
+        torch.cuda.synchronize()
+        assert torch.equal(og, oe)
+        assert torch.equal(graphed.state, eager.state)
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(graphed.ring_tensors(), eager.ring_tensors()))
+        assert np.array_equal(graphed.meta_array(), eager.meta_array())
+    assert device_errors(graphed) == 0 and device_errors(eager) == 0
