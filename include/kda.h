@@ -173,8 +173,9 @@ kda_status kda_prefill_noalloc(kda_pool* pool, const kda_prefill_args* args, voi
  * sequences ranked rank_end[i-1] .. rank_end[i] - 1 by length (longest first, ties: lower index
  * first; rank_end[-1] = 0) run in work-groups of vsw[i] value columns (16, 32, 64 or 128).
  * Long chains take narrow slices, short ones wide slices, by a latency / CU-time model; one
- * group beyond 64 sequences, and kda_mixed_batch always uses one group. Host only; returns 0
- * for a null argument or n_seq <= 0.                                                         */
+ * group beyond 64 sequences. kda_prefill, kda_prefill_noalloc and the prefill part of
+ * kda_mixed_batch all follow this plan. Host only; returns 0 for a null argument or
+ * n_seq <= 0.                                                                                */
 int32_t kda_prefill_plan(const kda_pool* pool, int32_t n_seq, const int32_t* h_cu_seqlens,
                          int32_t* rank_end, int32_t* vsw);
 
