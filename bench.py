@@ -246,8 +246,9 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if TimingEvent._hip is not None and self.h:
-            TimingEvent._hip.hipEventDestroy(self.h)
+        hip = type(self)._hip   # not the module global, which may be gone at interpreter exit
+        if hip is not None and self.h:
+            hip.hipEventDestroy(self.h)
 
 
 class Cold:

@@ -111,8 +111,9 @@ class _StreamEvent:
         self.handle = h.value
 
     def __del__(self):
-        if getattr(self, "handle", None) and _StreamEvent._hip is not None:
-            _StreamEvent._hip.hipEventDestroy(self.handle)
+        hip = type(self)._hip   # not the module global, which may be gone at interpreter exit
+        if getattr(self, "handle", None) and hip is not None:
+            hip.hipEventDestroy(self.handle)
             self.handle = None
 
 
