@@ -403,3 +403,136 @@ def test_mixed_batch_validation_errors_change_nothing():
     m.n_decode = -1
     assert lib.kda_mixed_batch(p.h, byref(m), None) == _abi.KDA_EINVAL
     assert states() == before
+
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_validation_fuzz_rejects_and_keeps_host_state(d):
+    """Random prefill, decode, verify, commit and rollback calls, each a valid call with one
+    certainly-invalid field drawn at random (slot out of range, free, repeated, or written
+    twice; broken cu_seqlens or n_tok; wrong chunk; negative interval; missing or misaligned
+    tensor, slot array or workspace; position count out of range; commit or rollback of idle
+    slots): every call is refused before any device work (neither OK nor a HIP error), and no
+    slot's host state changes. The host-sanitizer test runs this under ASan and UBSan too."""
+    rng = np.random.default_rng(4242 + d)
+    n, R, chunk = 24, 9, (16 if d == 16 else 64)
+    p = HostPool(n=n, H=2, d=d, R=R)
+    live = [p.alloc()[1] for _ in range(20)]      # slots 20..23 stay free
+    free_slots = [20, 21, 22, 23]
+    before = [lib.kda_slot_host_state(p.h, s) for s in range(n)]
+    refused = (_abi.KDA_OK, _abi.KDA_EHIP)
+
+    def unchanged():
+        assert [lib.kda_slot_host_state(p.h, s) for s in range(n)] == before
+
+    for _ in range(300):
+        n_seq = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 300, size=n_seq)]
+        lens[0] = max(lens[0], 1)
+        interval = int(rng.choice([0, chunk, 100]))
+        n_ck = sum(L // interval for L in lens) if interval else 0
+        if n_seq + n_ck > 20:
+            interval, n_ck = 0, 0
+        perm = [int(x) for x in rng.permutation(live)]
+        out = i32(*perm[:n_seq])
+        ck = i32(*perm[n_seq:n_seq + n_ck]) if n_ck else None
+        rest = perm[n_seq + n_ck:]
+        init = i32(*[rest[i] if i < len(rest) and rng.random() < 0.5 else -1 for i in range(n_seq)])
+        cu = i32(0, *np.cumsum(lens))
+        a = prefill_args(cu, out, init, ck, chunk=chunk, interval=interval)
+        need = lib.kda_prefill_workspace_bytes(p.h, int(cu[-1]), n_seq, chunk, interval)
+        a.workspace, a.workspace_bytes = FAKE, need
+        # what these lengths need exactly (the plan arrays, then one block per chunk and head;
+        # an interval that is not a multiple of the chunk cuts every interval into
+        # ceil(interval / chunk) chunks): kda_prefill_workspace_bytes bounds it from above
+        if need:
+            per = -(-interval // chunk)
+            chunks = sum(-(-L // chunk) if interval % chunk == 0 else
+                         (L // interval) * per - (-(L % interval) // chunk) for L in lens)
+            exact = -(-4 * (3 * n_seq + 1) // 256) * 256 + chunks * 2 * 61952
+            assert exact <= need
+        kinds = ["out_range", "out_free", "cu0", "ntok", "chunk", "interval", "null_q",
+                 "misaligned_o", "null_cu", "init_free", "init_half"]
+        if n_seq >= 2:
+            kinds += ["out_dup", "init_other_out", "cu_decrease"]
+        if n_ck:
+            kinds += ["ck_dup_out", "ck_missing"]
+        if need > 0:
+            kinds += ["ws_small", "ws_null", "ws_misaligned"]
+        kind = kinds[int(rng.integers(0, len(kinds)))]
+        if kind == "out_range":
+            out[int(rng.integers(0, n_seq))] = int(rng.choice([-2, n, n + 7, 1 << 30]))
+        elif kind == "out_free":
+            out[int(rng.integers(0, n_seq))] = free_slots[int(rng.integers(0, 4))]
+        elif kind == "out_dup":
+            out[1] = out[0]
+        elif kind == "init_other_out":
+            init[1] = out[0]
+        elif kind == "init_free":
+            init[0] = free_slots[int(rng.integers(0, 4))]
+        elif kind == "init_half":
+            a.d_init_slot = None
+        elif kind == "cu0":
+            cu[0] = 1
+        elif kind == "cu_decrease":
+            cu[1] = cu[2] + 1
+        elif kind == "ntok":
+            a.n_tok = int(cu[-1]) + int(rng.integers(1, 100))
+        elif kind == "chunk":
+            a.chunk = chunk * 2
+        elif kind == "interval":
+            a.ckpt_interval = -int(rng.integers(1, 1000))
+        elif kind == "null_q":
+            a.q = None
+        elif kind == "misaligned_o":
+            a.o = FAKE + 8
+        elif kind == "null_cu":
+            a.h_cu_seqlens = None
+        elif kind == "ck_dup_out":
+            ck[0] = out[0]
+        elif kind == "ck_missing":
+            a.h_ckpt_slot = None
+        elif kind == "ws_small":
+            a.workspace_bytes = exact - 1
+        elif kind == "ws_null":
+            a.workspace = None
+        elif kind == "ws_misaligned":
+            a.workspace = FAKE + 16
+        st = lib.kda_prefill(p.h, byref(a), None)
+        assert st not in refused, (kind, st)
+        unchanged()
+
+        B = int(rng.integers(1, 5))
+        slots = i32(*[int(x) for x in rng.choice(live, size=B, replace=False)])
+        sa = step_args(B, slots)
+        kinds = ["range", "free", "b_neg", "null_h", "null_d", "null_q", "misaligned_k",
+                 "npos0", "npos_big", "commit_idle", "rollback_idle"] + (["dup"] if B >= 2 else [])
+        kind = kinds[int(rng.integers(0, len(kinds)))]
+        call = "decode" if kind not in ("npos0", "npos_big") else "verify"
+        if kind == "range":
+            slots[int(rng.integers(0, B))] = int(rng.choice([-1, n, 1 << 20]))
+        elif kind == "free":
+            slots[int(rng.integers(0, B))] = free_slots[int(rng.integers(0, 4))]
+        elif kind == "dup":
+            slots[1] = slots[0]
+        elif kind == "b_neg":
+            sa.B = -int(rng.integers(1, 5))
+        elif kind == "null_h":
+            sa.h_slots = None
+        elif kind == "null_d":
+            sa.d_slots = None
+        elif kind == "null_q":
+            sa.q = None
+        elif kind == "misaligned_k":
+            sa.k = FAKE + 4
+        if kind == "commit_idle":
+            st = lib.kda_commit(p.h, B, slots.ctypes.data, FAKE, FAKE, None)
+        elif kind == "rollback_idle":
+            st = lib.kda_rollback(p.h, B, slots.ctypes.data, FAKE, None)
+        elif call == "verify":
+            st = lib.kda_verify(p.h, byref(sa), 0 if kind == "npos0" else R + 1, None)
+        elif rng.random() < 0.5:
+            st = lib.kda_decode(p.h, byref(sa), None)
+        else:
+            st = lib.kda_verify(p.h, byref(sa), int(rng.integers(1, R + 1)), None)
+        assert st not in refused, (kind, st)
+        unchanged()
