@@ -536,3 +536,70 @@ def test_validation_fuzz_rejects_and_keeps_host_state(d):
             st = lib.kda_verify(p.h, byref(sa), int(rng.integers(1, R + 1)), None)
         assert st not in refused, (kind, st)
         unchanged()
+
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_mixed_batch_validation_fuzz(d):
+    """Random kda_mixed_batch calls, each a valid batch (prompts, decodes, verifies, optional
+    side stream) with one certainly-invalid choice drawn at random: a decode or verify slot that
+    is also a prefill out or init slot, a decode slot repeated as a verify slot, a commit of idle
+    slots, a free or out-of-range step slot, a position count out of range, a side stream with
+    a missing event, a null packed tensor or device slot array: every call is refused before
+    any device work and no slot's host state changes."""
+    rng = np.random.default_rng(777 + d)
+    n, R, chunk = 24, 9, (16 if d == 16 else 64)
+    p = HostPool(n=n, H=2, d=d, R=R)
+    live = [p.alloc()[1] for _ in range(20)]
+    before = [lib.kda_slot_host_state(p.h, s) for s in range(n)]
+    for _ in range(300):
+        perm = [int(x) for x in rng.permutation(live)]
+        n_seq, nd, nv = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        out, dec, ver = perm[:n_seq], perm[n_seq:n_seq + nd], perm[n_seq + nd:n_seq + nd + nv]
+        spare = perm[n_seq + nd + nv:]
+        init = [spare[0] if rng.random() < 0.5 else -1] + [-1] * (n_seq - 1)
+        lens = [int(x) for x in rng.integers(1, 200, size=n_seq)]
+        cu = i32(0, *np.cumsum(lens))
+        kinds = ["dec_is_out", "ver_is_out", "dec_is_ver", "commit_idle", "dec_free", "ver_range",
+                 "npos0", "npos_big", "fork_missing", "join_missing", "null_q", "null_dver"]
+        if init[0] >= 0:
+            kinds += ["dec_is_init", "ver_is_init"]
+        kind = kinds[int(rng.integers(0, len(kinds)))]
+        com = None
+        n_pos = int(rng.integers(1, R + 1))
+        if kind == "dec_is_out":
+            dec[0] = out[0]
+        elif kind == "ver_is_out":
+            ver[0] = out[int(rng.integers(0, n_seq))]
+        elif kind == "dec_is_init":
+            dec[0] = init[0]
+        elif kind == "ver_is_init":
+            ver[0] = init[0]
+        elif kind == "dec_is_ver":
+            dec[0] = ver[0]
+        elif kind == "commit_idle":
+            com = [spare[-1]]
+        elif kind == "dec_free":
+            dec[0] = int(rng.integers(20, 24))
+        elif kind == "ver_range":
+            ver[0] = int(rng.choice([-1, n, 1 << 16]))
+        elif kind == "npos0":
+            n_pos = 0
+        elif kind == "npos_big":
+            n_pos = R + 1
+        m, _keep = mixed_args(cu, i32(*out), dec=dec, ver=ver, n_pos=n_pos, com=com,
+                              init=i32(*init), chunk=chunk)
+        ws_need = lib.kda_prefill_workspace_bytes(p.h, int(cu[-1]), n_seq, chunk, 0)
+        m.prefill.workspace, m.prefill.workspace_bytes = FAKE, ws_need
+        if rng.random() < 0.5 or kind in ("fork_missing", "join_missing"):
+            m.side_stream, m.fork_event, m.join_event = FAKE, FAKE, FAKE
+        if kind == "fork_missing":
+            m.fork_event = None
+        elif kind == "join_missing":
+            m.join_event = None
+        elif kind == "null_q":
+            m.q = None
+        elif kind == "null_dver":
+            m.d_verify_slots = None
+        st = lib.kda_mixed_batch(p.h, byref(m), None)
+        assert st not in (_abi.KDA_OK, _abi.KDA_EHIP), (kind, st)
+        assert [lib.kda_slot_host_state(p.h, s) for s in range(n)] == before, kind
