@@ -1721,3 +1721,23 @@ def test_mixed_step_replayed_from_a_captured_graph():
         assert all(torch.equal(a_, b_) for a_, b_ in zip(graphed.ring_tensors(), eager.ring_tensors()))
         assert np.array_equal(graphed.meta_array(), eager.meta_array())
     assert device_errors(graphed) == 0 and device_errors(eager) == 0
+
+
+def test_readme_python_example_runs():
+    """The Python example in README.md runs as printed and leaves the slot metadata it shows."""
+    import contextlib
+    import io
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    readme = os.path.join(root, "README.md")
+    if not os.path.exists(readme):
+        pytest.skip("README.md is not in this copy of the tree")
+    text = open(readme).read()
+    code = re.search(r"```python\n(.*?)```", text, re.S).group(1)
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        exec(compile(code, "README.md", "exec"), {})
+    line = buf.getvalue().strip().splitlines()[-1]
+    assert "torch.Size([1000, 8, 128]) torch.Size([1, 8, 128]) torch.Size([1, 5, 8, 128])" in line
+    assert re.sub(r"\s+", " ", line).endswith("[1004 3 0 0 5]"), line
